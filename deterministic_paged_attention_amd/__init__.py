@@ -1,0 +1,370 @@
+"""Python binding of libbi.so (batch-invariant paged attention, RMSNorm, GEMM).
+
+Argument marshalling only: every step of the computation runs in the HIP
+kernels of libbi.so.  Functions carry the names of the C entry points in
+``include/bi.h``; tensors are torch tensors on the GPU (torch provides device
+memory and the current stream, nothing else).  Importing this package fails
+loudly when the library has not been built: there is no fallback path.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import numpy as np
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libbi.so")
+HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "bi.h")
+
+if not os.path.exists(LIB_PATH):
+    raise ImportError(f"{LIB_PATH} is missing: build it first with "
+                      "`python -m deterministic_paged_attention_amd.build` (or __graft_entry__.build())")
+
+lib = ctypes.CDLL(LIB_PATH)
+
+c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p
+P_i32 = ctypes.POINTER(ctypes.c_int32)
+
+BI_OK = 0
+STATUS_NAMES = {0: "BI_OK", 1: "BI_ERR_INVALID_ARG", 2: "BI_ERR_UNSUPPORTED_CONFIG", 3: "BI_ERR_OUT_OF_RANGE",
+                4: "BI_ERR_WRITE_CONFLICT", 5: "BI_ERR_WORKSPACE_TOO_SMALL", 6: "BI_ERR_HIP"}
+BI_BF16, BI_F32 = 0, 1
+
+
+class bi_attn_desc(ctypes.Structure):
+    _fields_ = [("num_q_heads", c_i32), ("num_kv_heads", c_i32), ("head_dim", c_i32), ("page_size", c_i32),
+                ("split_size", c_i32), ("window", c_i32), ("scale", c_f32)]
+
+
+class BiError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        self.status = status
+        self.status_name = STATUS_NAMES.get(status, str(status))
+        super().__init__(f"{self.status_name}: {message}")
+
+
+def _sig(name, restype, *argtypes):
+    f = getattr(lib, name)
+    f.restype = restype
+    f.argtypes = list(argtypes)
+    return f
+
+
+_sig("bi_attn_config_create", c_i32, ctypes.POINTER(bi_attn_desc), ctypes.POINTER(c_vp))
+_sig("bi_attn_config_destroy", None, c_vp)
+_sig("bi_attn_config_query", c_i32, c_vp, ctypes.POINTER(bi_attn_desc), P_i32)
+_sig("bi_kv_cache_bytes", c_i32, c_vp, c_i64, ctypes.POINTER(c_sz))
+_sig("bi_slot_mapping", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp)
+_sig("bi_kv_write", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp)
+_sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, ctypes.POINTER(c_sz))
+_ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
+_sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
+_sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
+_sig("bi_paged_attention_merge", c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp)
+_sig("bi_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c_vp)
+_sig("bi_gemm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_vp)
+_sig("bi_check_page_table", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
+_sig("bi_check_write_plan", c_i32, c_vp, c_i32, c_vp, c_i32, c_i32)
+_sig("bi_splitk_attention_heuristic", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, P_i32)
+_sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
+_sig("bi_paged_attention_splitk", c_i32, *_ATTN_ARGS, c_i32, c_vp, c_sz, c_vp, c_vp)
+_sig("bi_gemm_splitk_heuristic", c_i32, c_i64)
+_sig("bi_gemm_splitk_workspace_size", c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_sz))
+_sig("bi_gemm_splitk", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_i32, c_vp, c_sz,
+     c_vp)
+_sig("bi_status_string", ctypes.c_char_p, c_i32)
+_sig("bi_last_error_message", ctypes.c_char_p)
+_sig("bi_version", c_i32)
+
+
+def _check(status: int) -> None:
+    if status != BI_OK:
+        raise BiError(status, lib.bi_last_error_message().decode())
+
+
+def declared_functions(header: str = HEADER_PATH):
+    """Names of the functions include/bi.h declares (used by the export test)."""
+    text = open(header).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(bi_[a-z0-9_]+)\s*\(", text)))
+
+
+# ---------------------------------------------------------------------------
+# torch marshalling helpers
+# ---------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _stream(stream=None) -> int:
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _need(t, dtype, name, device=True):
+    torch = _torch()
+    if t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, got {t.dtype}")
+    if device and t.device.type != "cuda":
+        raise TypeError(f"{name} must be a GPU tensor")
+
+
+def _row_stride(t, name):
+    """Element stride between rows of a [rows, ...] view whose trailing dims are contiguous."""
+    inner = 1
+    for d in range(t.dim() - 1, 0, -1):
+        if t.stride(d) != inner:
+            raise ValueError(f"{name}: trailing dimensions must be contiguous")
+        inner *= t.shape[d]
+    return t.stride(0) if t.shape[0] > 1 else max(inner, t.stride(0))
+
+
+class AttnConfig:
+    """Owns a bi_attn_config handle (bi_attn_config_create / _destroy)."""
+
+    def __init__(self, num_q_heads, num_kv_heads, head_dim, page_size=16, split_size=256, window=0, scale=0.0):
+        d = bi_attn_desc(num_q_heads, num_kv_heads, head_dim, page_size, split_size, window, float(scale))
+        h = c_vp()
+        _check(lib.bi_attn_config_create(ctypes.byref(d), ctypes.byref(h)))
+        self.handle = h
+        q = bi_attn_desc()
+        tile = c_i32()
+        _check(lib.bi_attn_config_query(self.handle, ctypes.byref(q), ctypes.byref(tile)))
+        self.desc = q
+        self.key_tile = tile.value
+        self.num_q_heads, self.num_kv_heads, self.head_dim = num_q_heads, num_kv_heads, head_dim
+        self.page_size, self.split_size, self.window, self.scale = page_size, split_size, window, q.scale
+
+    def __del__(self):
+        h = getattr(self, "handle", None)
+        if h is not None and h.value:
+            lib.bi_attn_config_destroy(h)
+            self.handle = None
+
+    def k_cache_shape(self, num_pages) -> Tuple[int, ...]:
+        return (num_pages, self.num_kv_heads, self.head_dim // 8, self.page_size, 8)
+
+    def v_cache_shape(self, num_pages) -> Tuple[int, ...]:
+        return (num_pages, self.num_kv_heads, self.head_dim, self.page_size)
+
+
+def bi_attn_config_create(num_q_heads, num_kv_heads, head_dim, page_size=16, split_size=256, window=0, scale=0.0):
+    return AttnConfig(num_q_heads, num_kv_heads, head_dim, page_size, split_size, window, scale)
+
+
+def bi_kv_cache_bytes(cfg: AttnConfig, num_pages: int) -> int:
+    b = c_sz()
+    _check(lib.bi_kv_cache_bytes(cfg.handle, num_pages, ctypes.byref(b)))
+    return b.value
+
+
+def bi_slot_mapping(page_table, seq_lens, query_start_loc, num_tokens, page_size, num_pages, out=None, stream=None):
+    torch = _torch()
+    for t, n in ((page_table, "page_table"), (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc")):
+        _need(t, torch.int32, n)
+    if out is None:
+        out = torch.empty(num_tokens, dtype=torch.int32, device=page_table.device)
+    _need(out, torch.int32, "out")
+    assert page_table.is_contiguous()
+    _check(lib.bi_slot_mapping(_ptr(page_table), page_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc),
+                               seq_lens.shape[0], num_tokens, page_size, num_pages, _ptr(out), _stream(stream)))
+    return out
+
+
+def bi_kv_write(cfg: AttnConfig, k_new, v_new, slot_mapping, k_cache, v_cache, stream=None):
+    torch = _torch()
+    _need(k_new, torch.bfloat16, "k_new")
+    _need(v_new, torch.bfloat16, "v_new")
+    _need(slot_mapping, torch.int32, "slot_mapping")
+    n = k_new.shape[0]
+    _check(lib.bi_kv_write(cfg.handle, _ptr(k_new), _row_stride(k_new, "k_new") if n else cfg.num_kv_heads * cfg.head_dim,
+                           _ptr(v_new), _row_stride(v_new, "v_new") if n else cfg.num_kv_heads * cfg.head_dim,
+                           _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(stream)))
+
+
+def bi_paged_attention_workspace_size(cfg: AttnConfig, num_tokens: int, max_seq_len: int) -> int:
+    b = c_sz()
+    _check(lib.bi_paged_attention_workspace_size(cfg.handle, num_tokens, max_seq_len, ctypes.byref(b)))
+    return b.value
+
+
+def bi_paged_attention_splitk_workspace_size(cfg: AttnConfig, num_tokens: int, max_seq_len: int, num_splits: int):
+    b = c_sz()
+    _check(lib.bi_paged_attention_splitk_workspace_size(cfg.handle, num_tokens, max_seq_len, num_splits,
+                                                        ctypes.byref(b)))
+    return b.value
+
+
+def alloc_workspace(nbytes: int, device="cuda"):
+    torch = _torch()
+    return torch.empty(max(nbytes, 16), dtype=torch.uint8, device=device)
+
+
+def _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc):
+    torch = _torch()
+    _need(q, torch.bfloat16, "q")
+    _need(k_cache, torch.bfloat16, "k_cache")
+    _need(v_cache, torch.bfloat16, "v_cache")
+    for t, nm in ((page_table, "page_table"), (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc")):
+        _need(t, torch.int32, nm)
+    if not (page_table.is_contiguous() and k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("page_table and caches must be contiguous")
+    T = q.shape[0]
+    qs = _row_stride(q, "q") if T else cfg.num_q_heads * cfg.head_dim
+    return (cfg.handle, _ptr(q), qs, _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _ptr(page_table),
+            page_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc), seq_lens.shape[0], T)
+
+
+def bi_paged_attention(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_lens, query_start_loc, max_seq_len,
+                       workspace=None, out=None, stream=None):
+    torch = _torch()
+    args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
+    T = q.shape[0]
+    if workspace is None:
+        workspace = alloc_workspace(bi_paged_attention_workspace_size(cfg, T, max_seq_len), q.device)
+    if out is None:
+        out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+    _check(lib.bi_paged_attention(*args, max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                                  _ptr(out), _stream(stream)))
+    return out
+
+
+def bi_paged_attention_split(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_lens, query_start_loc,
+                             max_seq_len, workspace, stream=None):
+    args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
+    _check(lib.bi_paged_attention_split(*args, max_seq_len, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _stream(stream)))
+
+
+def bi_paged_attention_merge(cfg: AttnConfig, seq_lens, query_start_loc, num_tokens, max_seq_len, workspace,
+                             out=None, stream=None):
+    torch = _torch()
+    if out is None:
+        out = torch.empty((num_tokens, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=seq_lens.device)
+    _check(lib.bi_paged_attention_merge(cfg.handle, _ptr(seq_lens), _ptr(query_start_loc), seq_lens.shape[0],
+                                        num_tokens, max_seq_len, _ptr(workspace),
+                                        workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    return out
+
+
+def workspace_views(cfg: AttnConfig, workspace, num_tokens: int, num_splits: int):
+    """(ml [R, NS, 2] fp32, acc [R, NS, D] fp32) views of a workspace, per the layout in bi.h."""
+    torch = _torch()
+    R = num_tokens * cfg.num_q_heads
+    ml_bytes = R * num_splits * 8
+    acc_off = (ml_bytes + 255) // 256 * 256
+    f = workspace.view(torch.uint8)
+    ml = f[:ml_bytes].view(torch.float32).view(R, num_splits, 2)
+    acc = f[acc_off: acc_off + R * num_splits * cfg.head_dim * 4].view(torch.float32).view(R, num_splits, cfg.head_dim)
+    return ml, acc
+
+
+def bi_splitk_attention_heuristic(cfg: AttnConfig, num_seqs, max_seq_len, num_compute_units, waves_per_cu=8):
+    n = c_i32()
+    _check(lib.bi_splitk_attention_heuristic(cfg.handle, num_seqs, max_seq_len, num_compute_units, waves_per_cu,
+                                             ctypes.byref(n)))
+    return n.value
+
+
+def bi_paged_attention_splitk(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_lens, query_start_loc,
+                              max_seq_len, num_splits, workspace=None, out=None, stream=None):
+    torch = _torch()
+    args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
+    T = q.shape[0]
+    if workspace is None:
+        workspace = alloc_workspace(bi_paged_attention_splitk_workspace_size(cfg, T, max_seq_len, num_splits),
+                                    q.device)
+    if out is None:
+        out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+    _check(lib.bi_paged_attention_splitk(*args, max_seq_len, num_splits, _ptr(workspace),
+                                         workspace.numel() * workspace.element_size(), _ptr(out), _stream(stream)))
+    return out
+
+
+def bi_rmsnorm(x, gamma, eps, out=None, stream=None):
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    _need(gamma, torch.bfloat16, "gamma")
+    M, H = x.shape
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=x.device)
+    ldx = x.stride(0) if M > 1 else H
+    ldy = out.stride(0) if M > 1 else H
+    if x.stride(1) != 1 or out.stride(1) != 1 or not gamma.is_contiguous():
+        raise ValueError("rows of x / out and gamma must be contiguous")
+    _check(lib.bi_rmsnorm(_ptr(x), ldx, _ptr(gamma), float(eps), M, H, _ptr(out), ldy, _stream(stream)))
+    return out
+
+
+def _gemm_args(a, w, out, out_dtype):
+    torch = _torch()
+    _need(a, torch.bfloat16, "a")
+    _need(w, torch.bfloat16, "w")
+    M, K = a.shape
+    N = w.shape[0]
+    if out is None:
+        out = torch.empty((M, N), dtype=out_dtype, device=a.device)
+    if a.stride(1) != 1 or w.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("a, w and out need contiguous rows")
+    dt = BI_F32 if out.dtype == torch.float32 else BI_BF16
+    if out.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("out must be bf16 or fp32")
+    lda = a.stride(0) if M > 1 else K
+    ldw = w.stride(0) if N > 1 else K
+    ldc = out.stride(0) if M > 1 else N
+    return out, (_ptr(a), lda, _ptr(w), ldw, _ptr(out), ldc, dt, M, N, K)
+
+
+def bi_gemm(a, w, out_dtype=None, out=None, stream=None):
+    torch = _torch()
+    out, args = _gemm_args(a, w, out, out_dtype or torch.bfloat16)
+    _check(lib.bi_gemm(*args, _stream(stream)))
+    return out
+
+
+def bi_gemm_splitk_heuristic(M: int) -> int:
+    return lib.bi_gemm_splitk_heuristic(M)
+
+
+def bi_gemm_splitk(a, w, k_splits, out_dtype=None, out=None, workspace=None, stream=None):
+    torch = _torch()
+    out, args = _gemm_args(a, w, out, out_dtype or torch.bfloat16)
+    M, N = out.shape
+    need = c_sz()
+    _check(lib.bi_gemm_splitk_workspace_size(M, N, k_splits, ctypes.byref(need)))
+    if workspace is None:
+        workspace = alloc_workspace(need.value, a.device)
+    _check(lib.bi_gemm_splitk(*args, k_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
+                              _stream(stream)))
+    return out
+
+
+def bi_check_page_table(page_table, seq_lens, query_start_loc, page_size, num_pages):
+    """Host check of a page table (numpy / list inputs); raises BiError."""
+    pt = np.ascontiguousarray(np.asarray(page_table, dtype=np.int32))
+    sl = np.ascontiguousarray(np.asarray(seq_lens, dtype=np.int32))
+    qsl = None if query_start_loc is None else np.ascontiguousarray(np.asarray(query_start_loc, dtype=np.int32))
+    _check(lib.bi_check_page_table(pt.ctypes.data, pt.shape[1], sl.ctypes.data,
+                                   None if qsl is None else qsl.ctypes.data, sl.shape[0], page_size, num_pages))
+
+
+def bi_check_write_plan(slot_mapping, page_writable, num_pages, page_size):
+    """Host check of a write plan (numpy / list inputs); raises BiError."""
+    sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int32))
+    pw = None if page_writable is None else np.ascontiguousarray(np.asarray(page_writable, dtype=np.uint8))
+    _check(lib.bi_check_write_plan(sm.ctypes.data if sm.size else None, sm.shape[0],
+                                   None if pw is None else pw.ctypes.data, num_pages, page_size))
+
+
+def bi_version() -> int:
+    return lib.bi_version()

@@ -1,0 +1,81 @@
+// Internal declarations shared by the C-ABI layer (api.hip) and the kernel
+// translation units.  Not part of the public interface.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace bi {
+
+// Largest query-row block: the 16 columns of one 16x16 MFMA output.
+constexpr int kRowsPerBlock = 16;
+// Key tile: two pages of 16 tokens, the K extent of one 16x16x32 MFMA.
+constexpr int kKeyTile = 32;
+// Waves per attention workgroup; each wave owns one key split.
+constexpr int kSplitWaves = 4;
+
+struct AttnSplitArgs {
+  const uint16_t* q;
+  int64_t q_stride;          // elements between token rows of q
+  const uint16_t* k_cache;
+  const uint16_t* v_cache;
+  const int32_t* page_table;
+  int32_t pt_stride;
+  int32_t num_pages;
+  const int32_t* seq_lens;
+  const int32_t* qsl;        // query_start_loc [num_seqs + 1]
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t log2_group;        // log2(H_q / H_kv)
+  int32_t split;             // keys per split (multiple of kKeyTile)
+  int32_t window;            // 0 = none
+  int32_t ns;                // splits per row in the workspace
+  float qk_scale_log2;       // scale * log2(e)
+  float2* ws_ml;             // [R][ns]
+  float* ws_acc;             // [R][ns][D]
+};
+
+struct AttnMergeArgs {
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  int32_t num_tokens;
+  int32_t num_q_heads;
+  int32_t split;
+  int32_t window;
+  int32_t ns;
+  const float2* ws_ml;
+  const float* ws_acc;
+  uint16_t* out;             // bf16 [T][H_q][D]
+};
+
+hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t stream);
+hipError_t launch_attn_merge(int head_dim, const AttnMergeArgs& a, hipStream_t stream);
+
+hipError_t launch_slot_mapping(const int32_t* page_table, int32_t stride, const int32_t* seq_lens,
+                               const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
+                               int32_t page_size, int32_t num_pages, int32_t* slots,
+                               hipStream_t stream);
+
+hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
+                           const uint16_t* v_new, int64_t v_stride, const int32_t* slots,
+                           int32_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
+                           int32_t num_pages, hipStream_t stream);
+
+hipError_t launch_rmsnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
+                          int64_t M, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);
+
+// out_kind: 0 = bf16, 1 = fp32.  k range [k_begin, k_begin + k_len_per_split) per
+// blockIdx.z when k_splits > 1 (partials to fp32 [k_splits][M][N], ldc = N).
+hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c,
+                       int64_t ldc, int out_kind, int64_t M, int64_t N, int64_t K,
+                       hipStream_t stream);
+hipError_t launch_gemm_splitk(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw,
+                              float* partial, int64_t M, int64_t N, int64_t K, int32_t k_splits,
+                              hipStream_t stream);
+hipError_t launch_gemm_splitk_reduce(const float* partial, int32_t k_splits, int64_t M, int64_t N,
+                                     void* c, int64_t ldc, int out_kind, hipStream_t stream);
+
+}  // namespace bi

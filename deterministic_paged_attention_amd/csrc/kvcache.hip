@@ -1,0 +1,114 @@
+// Slot mapping and KV write for the paged cache.
+//
+// Vosti deep-dive blog (深入解析 Vosti), §3.2: invariant 1 (page tables map a
+// request's prefix to allocated, in-range slots), invariant 2 and §5.1 (the
+// KV value stored for position p is that logical position's value whatever
+// page holds it), invariant 3 (a step writes only private, pairwise distinct
+// slots; checked on the host by bi_check_write_plan).  Both kernels are pure
+// integer addressing and copies, so they are bit-exact by construction.
+
+#include "bi_internal.h"
+
+namespace bi {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_table, int32_t stride,
+                                                           const int32_t* seq_lens, const int32_t* qsl,
+                                                           int32_t num_seqs, int32_t num_tokens,
+                                                           int32_t page_size, int32_t num_pages,
+                                                           int32_t* slots) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= num_tokens) return;
+  const int s = find_token_seq(qsl, num_seqs, t);
+  const int q0 = qsl[s];
+  const int q_len = qsl[s + 1] - q0;
+  const int p = seq_lens[s] - q_len + (t - q0);
+  int slot = -1;
+  if (p >= 0 && t < qsl[s + 1]) {
+    const int lp = p / page_size;
+    if (lp < stride) {
+      const int pg = page_table[(int64_t)s * stride + lp];
+      if (pg >= 0 && pg < num_pages) slot = pg * page_size + p % page_size;
+    }
+  }
+  slots[t] = slot;
+}
+
+// One thread per (token, KV head, 8-element head-dim chunk c).
+// K cache [page][h][D/8][16][8]: the chunk is one 16-byte store.
+// V cache [page][h][D][16]:      eight 2-byte stores, one per head-dim row.
+template <int D>
+__global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
+                                                       const uint16_t* v_new, int64_t v_stride,
+                                                       const int32_t* slots, int32_t num_tokens,
+                                                       uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages) {
+  constexpr int NC = D / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * NC;
+  if (gid >= total) return;
+  const int c = (int)(gid % NC);
+  const int h = (int)((gid / NC) % num_kv_heads);
+  const int t = (int)(gid / ((int64_t)NC * num_kv_heads));
+  const int slot = slots[t];
+  if (slot < 0) return;
+  const int pg = slot >> 4;
+  const int o = slot & 15;
+  if (pg >= num_pages) return;
+  const int64_t head_base = ((int64_t)pg * num_kv_heads + h) * (D * 16);
+  const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + (int64_t)t * k_stride + h * D + 8 * c);
+  *reinterpret_cast<u32x4*>(k_cache + head_base + (c * 16 + o) * 8) = kv;
+  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + (int64_t)t * v_stride + h * D + 8 * c);
+  uint16_t* vd = v_cache + head_base + (int64_t)(8 * c) * 16 + o;
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    vd[(2 * e) * 16] = (uint16_t)(vv[e] & 0xffffu);
+    vd[(2 * e + 1) * 16] = (uint16_t)(vv[e] >> 16);
+  }
+}
+
+template <int D>
+hipError_t kv_write_launch(int num_kv_heads, const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
+                           int64_t v_stride, const int32_t* slots, int32_t num_tokens, uint16_t* k_cache,
+                           uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (D / 8);
+  if (total == 0) return hipSuccess;
+  hipLaunchKernelGGL(kv_write_kernel<D>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
+                     num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache,
+                     num_pages);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_slot_mapping(const int32_t* page_table, int32_t stride, const int32_t* seq_lens,
+                               const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
+                               int32_t page_size, int32_t num_pages, int32_t* slots, hipStream_t stream) {
+  if (num_tokens == 0) return hipSuccess;
+  hipLaunchKernelGGL(slot_mapping_kernel, dim3((num_tokens + 255) / 256), dim3(256), 0, stream, page_table,
+                     stride, seq_lens, qsl, num_seqs, num_tokens, page_size, num_pages, slots);
+  return hipGetLastError();
+}
+
+hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
+                           const uint16_t* v_new, int64_t v_stride, const int32_t* slots, int32_t num_tokens,
+                           uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 256: return kv_write_launch<256>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+}  // namespace bi

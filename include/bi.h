@@ -1,0 +1,284 @@
+/*
+ * bi.h — batch-invariant paged attention, RMSNorm and matrix product for
+ * AMD MI355X (gfx950).  C ABI of libbi.so.
+ *
+ * Property.  For the same token history every output row is bitwise identical
+ * whatever the batch composition, query length or chunk budget, decode versus
+ * prefill, physical page layout or prefix reuse (Vosti: Specifying,
+ * Implementing, and Verifying Deterministic LLM Inference, abstract; Vosti
+ * deep-dive blog (深入解析 Vosti), §6.1 matmul contract and §6.2 attention
+ * causal contract).  Invariance holds within one build of this library, one
+ * configuration and one GPU model; nothing is claimed across dtypes, kernel
+ * configurations, compiler versions or hardware (deep-dive blog, §3.5).
+ *
+ * Conventions for every function below.
+ *  - Pointers named *_dev are device pointers (HBM); the library never
+ *    allocates, frees or retains them.  Pointers named *_host are host memory.
+ *  - bf16 tensors are passed as raw 16-bit storage (void*), fp32 as float*.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Every launch is enqueued on it; no call synchronises the device.
+ *  - Arguments are validated on the host before anything is launched; an
+ *    invalid call launches nothing and returns a status.  Launch failures
+ *    return BI_ERR_HIP.  The text of the last error of the calling thread is
+ *    available from bi_last_error_message().
+ *  - Device-side data (page tables, lengths) is not read by the host.  Its
+ *    validity is a precondition, checkable on host copies with
+ *    bi_check_page_table / bi_check_write_plan.  The kernels stay memory-safe
+ *    when it is violated (out-of-range page ids are read as zero pages,
+ *    positions past the workspace bound are skipped) but the results of rows
+ *    that violate it are unspecified.
+ *  - No kernel uses atomics; no kernel communicates across workgroups.
+ */
+#ifndef BI_H_
+#define BI_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum bi_status {
+  BI_OK = 0,
+  BI_ERR_INVALID_ARG = 1,         /* null pointer, negative size, inconsistent shapes  */
+  BI_ERR_UNSUPPORTED_CONFIG = 2,  /* geometry this build has no kernel for: rejected  */
+  BI_ERR_OUT_OF_RANGE = 3,        /* a page id / slot / length outside its bound       */
+  BI_ERR_WRITE_CONFLICT = 4,      /* two writes to one slot, or a write to a shared page */
+  BI_ERR_WORKSPACE_TOO_SMALL = 5, /* caller's workspace below the size query's answer  */
+  BI_ERR_HIP = 6                  /* a HIP runtime call failed                          */
+} bi_status;
+
+typedef enum bi_dtype { BI_BF16 = 0, BI_F32 = 1 } bi_dtype;
+
+/* ------------------------------------------------------------------------ */
+/* Attention configuration.                                                  */
+/*                                                                           */
+/* Kernel choices are fixed once from the model geometry and never from the  */
+/* batch, chunk or prefill-vs-decode state; a geometry with no kernel is     */
+/* rejected, there is no runtime autotuning (Vosti deep-dive blog, §3.2,     */
+/* "fixed kernel choices").  The key split has a fixed SIZE, not a fixed     */
+/* number of splits (record "Deterministic and bit-exact inference", field   */
+/* technical, Invariance).                                                   */
+/* ------------------------------------------------------------------------ */
+typedef struct bi_attn_desc {
+  int32_t num_q_heads;   /* H_q; multiple of num_kv_heads                               */
+  int32_t num_kv_heads;  /* H_kv; G = H_q / H_kv must divide 16                          */
+  int32_t head_dim;      /* D in {64, 128, 256}                                          */
+  int32_t page_size;     /* P, tokens per page; this build supports 16                   */
+  int32_t split_size;    /* S, keys per split; a positive multiple of 32 (the key tile)  */
+  int32_t window;        /* w: 0 = full causal; w >= 1 = keys [max(0, p-w+1), p]         */
+  float scale;           /* softmax scale; 0 selects 1/sqrt(head_dim)                    */
+} bi_attn_desc;
+
+typedef struct bi_attn_config bi_attn_config; /* opaque, immutable after creation */
+
+/* Create a configuration.  Returns BI_ERR_UNSUPPORTED_CONFIG for a geometry
+ * this build has no kernel for and BI_ERR_INVALID_ARG for nonsense values.
+ * The handle is owned by the library (free with bi_attn_config_destroy) and
+ * may be shared by threads and streams. */
+bi_status bi_attn_config_create(const bi_attn_desc* desc, bi_attn_config** out);
+void bi_attn_config_destroy(bi_attn_config* cfg);
+/* Resolved descriptor (scale filled in) and the fixed key tile (32). */
+bi_status bi_attn_config_query(const bi_attn_config* cfg, bi_attn_desc* desc_out,
+                               int32_t* key_tile_out);
+
+/* ------------------------------------------------------------------------ */
+/* Paged KV cache layout (one layer), bf16, owned by the caller:             */
+/*   K: [num_pages][H_kv][D/8][P][8]   (8 head-dim elements of one token are */
+/*       contiguous; the 16 tokens of a page follow each other per 8-chunk)  */
+/*   V: [num_pages][H_kv][D][P]        (the P tokens of one head-dim index   */
+/*       are contiguous)                                                     */
+/* Page table: int32 [num_seqs][page_table_stride]; entry i of sequence s is */
+/* the physical page holding logical positions [i*P, (i+1)*P).  Entries past */
+/* ceil(k_len/P) are never read.                                             */
+/* Sequence metadata, device int32: seq_lens[s] = k_len (keys after this     */
+/* step's writes); query_start_loc[0..num_seqs] = prefix sums of q_len, with */
+/* 1 <= q_len <= k_len.  The new tokens of a sequence are its last q_len     */
+/* positions: row i sits at p = k_len - q_len + i (Vosti deep-dive blog,     */
+/* §6.2, attention causal contract).                                         */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes of one layer's K (or V) cache with num_pages pages. */
+bi_status bi_kv_cache_bytes(const bi_attn_config* cfg, int64_t num_pages, size_t* bytes);
+
+/* Slot mapping (Vosti deep-dive blog, §3.2, invariant 1: page tables map the
+ * prefix to allocated in-range slots).  For token t, row j of sequence s:
+ *   p = seq_lens[s] - q_len_s + j,
+ *   slot_mapping_dev[t] = page_table[s][p / P] * P + p % P,
+ * or -1 when the page id is outside [0, num_pages) or p / P >= stride.
+ * Outputs int32 [num_tokens]. */
+bi_status bi_slot_mapping(const int32_t* page_table_dev, int32_t page_table_stride,
+                          const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                          int32_t num_seqs, int32_t num_tokens, int32_t page_size,
+                          int32_t num_pages, int32_t* slot_mapping_dev, void* stream);
+
+/* KV write (deep-dive blog, §3.2 invariant 2 and §5.1: the value stored at
+ * the slot of position p is the value of that logical position).  Copies
+ * k_new[t] and v_new[t] ([H_kv][D] bf16, token rows `*_row_stride` elements
+ * apart) into slot slot_mapping[t] of the caches above; slots < 0 are
+ * skipped.  A pure copy: bit-exact.  The slots of one call must be distinct
+ * (write isolation, §3.2 invariant 3); check with bi_check_write_plan. */
+bi_status bi_kv_write(const bi_attn_config* cfg,
+                      const void* k_new_dev, int64_t k_row_stride,
+                      const void* v_new_dev, int64_t v_row_stride,
+                      const int32_t* slot_mapping_dev, int32_t num_tokens,
+                      void* k_cache_dev, void* v_cache_dev, int32_t num_pages, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Paged attention: decode and chunked prefill through one kernel.           */
+/*                                                                           */
+/* For query row at position p, head h, KV head g = h / G, keys j in         */
+/* [lo, p] (lo = max(0, p-w+1) if w > 0 else 0):                             */
+/*   o = sum_j softmax_j(scale * <q, k_j>) v_j      (deep-dive blog, §6.2)   */
+/* computed as fixed key splits [sS, (s+1)S), each a pass over 32-key tiles  */
+/* in increasing order with an online softmax, and a merge of the splits in  */
+/* increasing split order.  A tile in which a row has no visible key leaves  */
+/* that row's state bit-for-bit unchanged (deep-dive blog, §6.2, value rules */
+/* for fully masked tiles).  Output bf16 [num_tokens][H_q][D] contiguous,    */
+/* round-to-nearest-even, with -0 written as +0.                             */
+/*                                                                           */
+/* q: bf16 [num_tokens][H_q][D], token rows q_row_stride elements apart      */
+/* (>= H_q*D).  max_seq_len >= every seq_lens[s]; it sizes the grid and the  */
+/* workspace only.                                                           */
+/*                                                                           */
+/* Workspace (caller-owned device memory, contents scratch between calls):   */
+/*   NS = ceil(max_seq_len / S); R = num_tokens * H_q                        */
+/*   ml : float2 [R][NS]      (m, l) of each split, m in base-2 units:       */
+/*        m = max_j y_j, l = sum_j 2^(y_j - m), y_j = scale*log2(e)*<q,k_j>  */
+/*   acc: float  [R][NS][D]   sum_j 2^(y_j - m) v_j, starting at the first   */
+/*        256-byte boundary after ml                                         */
+/* Only the splits that meet [lo, p] of a row are written and read.          */
+/* ------------------------------------------------------------------------ */
+bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_tokens,
+                                            int32_t max_seq_len, size_t* bytes);
+
+bi_status bi_paged_attention(const bi_attn_config* cfg,
+                             const void* q_dev, int64_t q_row_stride,
+                             const void* k_cache_dev, const void* v_cache_dev, int32_t num_pages,
+                             const int32_t* page_table_dev, int32_t page_table_stride,
+                             const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                             int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                             void* workspace_dev, size_t workspace_bytes,
+                             void* out_dev, void* stream);
+
+/* The two phases of bi_paged_attention, separately: the split phase writes the
+ * workspace partials described above; the merge phase reads them and writes
+ * the output.  bi_paged_attention == split then merge on the same stream. */
+bi_status bi_paged_attention_split(const bi_attn_config* cfg,
+                                   const void* q_dev, int64_t q_row_stride,
+                                   const void* k_cache_dev, const void* v_cache_dev, int32_t num_pages,
+                                   const int32_t* page_table_dev, int32_t page_table_stride,
+                                   const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                   void* workspace_dev, size_t workspace_bytes, void* stream);
+
+bi_status bi_paged_attention_merge(const bi_attn_config* cfg,
+                                   const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                                   int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                   const void* workspace_dev, size_t workspace_bytes,
+                                   void* out_dev, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* RMSNorm, one row at a time (record "Deterministic and bit-exact           */
+/* inference", field technical, Invariance).                                 */
+/*   y[m,:] = x[m,:] * (sum_k x[m,k]^2 / H + eps)^(-1/2) * gamma             */
+/* fp32 sum of squares in a reduction tree fixed by H alone, fp32 scaling,   */
+/* one bf16 rounding.  x, y bf16 with row strides ld_x, ld_y (elements);     */
+/* gamma bf16 [H].  H must be a positive multiple of 8; in-place (x == y,    */
+/* same stride) is allowed.                                                  */
+/* ------------------------------------------------------------------------ */
+bi_status bi_rmsnorm(const void* x_dev, int64_t ld_x, const void* gamma_dev, float eps,
+                     int64_t M, int64_t H, void* y_dev, int64_t ld_y, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Matrix product with a K path fixed independently of M (Vosti deep-dive    */
+/* blog, §6.1, matmul contract and its obligations: zero-initialised         */
+/* accumulator, same-order iteration and reduction over a shared K).         */
+/*   c[m,n] = sum_k a[m,k] * w[n,k]                                          */
+/* a bf16 [M][K] (row stride lda), w bf16 [N][K] (row stride ldw), c [M][N]  */
+/* (row stride ldc) in bf16 or fp32.  bf16 MFMA, fp32 accumulation in one    */
+/* accumulator per output element, K visited in increasing 32-wide steps, no */
+/* split of K.  K must be a multiple of 32; lda, ldw multiples of 8.         */
+/* ------------------------------------------------------------------------ */
+bi_status bi_gemm(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw,
+                  void* c_dev, int64_t ldc, bi_dtype c_dtype,
+                  int64_t M, int64_t N, int64_t K, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Host-side plan checks (host arrays; nothing is launched).                 */
+/* ------------------------------------------------------------------------ */
+
+/* Every entry a sequence uses (indices < ceil(seq_lens[s]/P)) lies in
+ * [0, num_pages) and fits in the row (ceil(k_len/P) <= stride); also
+ * 1 <= q_len <= k_len when query_start_loc_host is non-NULL.
+ * BI_ERR_OUT_OF_RANGE otherwise (deep-dive blog, §3.2 invariant 1). */
+bi_status bi_check_page_table(const int32_t* page_table_host, int32_t page_table_stride,
+                              const int32_t* seq_lens_host, const int32_t* query_start_loc_host,
+                              int32_t num_seqs, int32_t page_size, int32_t num_pages);
+
+/* Slots in range and distinct, and none inside a page whose
+ * page_writable_host[page] is 0 (a shared prefix page is immutable; writable
+ * suffix slots are private; one plan's slots are disjoint: deep-dive blog,
+ * §3.2 invariant 3).  Negative slots are ignored.  BI_ERR_OUT_OF_RANGE or
+ * BI_ERR_WRITE_CONFLICT otherwise. */
+bi_status bi_check_write_plan(const int32_t* slot_mapping_host, int32_t num_tokens,
+                              const uint8_t* page_writable_host, int32_t num_pages,
+                              int32_t page_size);
+
+/* ------------------------------------------------------------------------ */
+/* Non-invariant comparators, for measurement only (never used by the        */
+/* invariant path).  The pages name split-K, whose reduction tree follows    */
+/* the shape, as what batch invariance gives up (LLM-42 summary, §1-§2).     */
+/* ------------------------------------------------------------------------ */
+
+/* Split count a batch-aware split-KV kernel would pick: enough work items to
+ * give every compute unit `waves_per_cu` of them.  The split length that
+ * follows, ceil(max_seq_len / num_splits) rounded up to the key tile, changes
+ * with the batch, and so does each row's reduction order. */
+bi_status bi_splitk_attention_heuristic(const bi_attn_config* cfg, int32_t num_seqs,
+                                        int32_t max_seq_len, int32_t num_compute_units,
+                                        int32_t waves_per_cu, int32_t* num_splits_out);
+
+bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_tokens,
+                                                   int32_t max_seq_len, int32_t num_splits,
+                                                   size_t* bytes);
+
+/* Same kernels as bi_paged_attention, with the split length derived from
+ * num_splits and max_seq_len instead of the configuration's fixed size. */
+bi_status bi_paged_attention_splitk(const bi_attn_config* cfg,
+                                    const void* q_dev, int64_t q_row_stride,
+                                    const void* k_cache_dev, const void* v_cache_dev, int32_t num_pages,
+                                    const int32_t* page_table_dev, int32_t page_table_stride,
+                                    const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                                    int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                    int32_t num_splits,
+                                    void* workspace_dev, size_t workspace_bytes,
+                                    void* out_dev, void* stream);
+
+/* k-splits a shape-aware GEMM would pick from M: 8 for M <= 16, 4 for
+ * M <= 128, else 1. */
+int32_t bi_gemm_splitk_heuristic(int64_t M);
+/* fp32 partial buffer [k_splits][M][N]. */
+bi_status bi_gemm_splitk_workspace_size(int64_t M, int64_t N, int32_t k_splits, size_t* bytes);
+/* K cut into k_splits equal 32-aligned ranges, each reduced separately, then
+ * summed in split order into c.  (K / 32) must be divisible by k_splits. */
+bi_status bi_gemm_splitk(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw,
+                         void* c_dev, int64_t ldc, bi_dtype c_dtype,
+                         int64_t M, int64_t N, int64_t K, int32_t k_splits,
+                         void* workspace_dev, size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Diagnostics.                                                              */
+/* ------------------------------------------------------------------------ */
+const char* bi_status_string(bi_status status);
+/* Message of the last failed call on this thread ("" if none). */
+const char* bi_last_error_message(void);
+/* Library ABI version (major*10000 + minor*100 + patch). */
+int32_t bi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* BI_H_ */

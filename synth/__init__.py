@@ -161,3 +161,24 @@ def chunk_schedule(total: int, budget: int, offset: int = 0) -> List[int]:
         out.append(n)
         rem -= n
     return out
+
+
+def normal_bf16_device(shape: Sequence[int], seed: int, device="cuda", std: float = 1.0,
+                       mean: float = 0.0) -> torch.Tensor:
+    """N(mean, std) bf16 drawn by torch's generator on the GPU (for full-size inputs
+    too large to draw on the host).  The bits are a fixed function of (seed, shape)
+    on a given device; a test that needs them on the host copies this tensor back
+    before any kernel under test has touched it."""
+    g = torch.Generator(device=device)
+    g.manual_seed(int(seed))
+    x = torch.randn(tuple(shape), generator=g, dtype=torch.float32, device=device)
+    if std != 1.0:
+        x.mul_(std)
+    if mean != 0.0:
+        x.add_(mean)
+    return x.to(torch.bfloat16)
+
+
+def llama8b_decode_lengths(batch: int, seed: int = 2000) -> List[int]:
+    """Context lengths of the 8B-shaped decode workload: k_len ~ U{512..8192}."""
+    return uniform_ints(batch, 512, 8192, seed)

@@ -1,0 +1,256 @@
+"""GPU parity: the HIP path (through the C ABI) against the CPU oracle.
+
+Tolerances: bf16 outputs max |gpu - oracle| <= 2e-2; fp32 GEMM outputs
+componentwise |gpu - oracle| <= 1e-3 * sum_k |a_k w_k|; integer and copy
+work bit-exact.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import deterministic_paged_attention_amd as bi
+import oracle
+import synth
+from harness import (DEV, PagedKV, Request, logical_k, logical_v, nan_cache, oracle_rows, page_table_tensor,
+                     run_step)
+
+pytestmark = pytest.mark.gpu
+BF16_TOL = 2e-2
+
+
+def _max_err(gpu_rows, ref_rows):
+    return max(float(np.max(np.abs(synth.to_f64(gpu_rows[k]) - ref_rows[k]))) for k in ref_rows)
+
+
+# ---------------------------------------------------------------- a1: slot mapping + KV write
+
+def test_slot_mapping_and_kv_write_bit_exact():
+    torch.manual_seed(0)
+    cfg = bi.AttnConfig(4, 2, 64)
+    geom = synth.Geometry(4, 2, 64, 16)
+    lengths, q_lens = [17, 33, 64, 100], [17, 5, 1, 37]
+    plan = synth.random_page_plan(lengths, 16, seed=3, slack=5)
+    pt_host = plan.table(stride=9).numpy()
+    pt_host[2, 3] = 999  # an entry beyond what sequence 2 uses: never read
+    pt = torch.tensor(pt_host, device=DEV)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    qsl_h = np.concatenate([[0], np.cumsum(q_lens)])
+    qsl = torch.tensor(qsl_h, dtype=torch.int32, device=DEV)
+    T = int(qsl_h[-1])
+    slots = bi.bi_slot_mapping(pt, sl, qsl, T, 16, plan.num_pages).cpu().numpy()
+    ref = oracle.slot_mapping_ref(pt_host, lengths, qsl_h, 16)
+    assert slots.tolist() == ref.tolist()
+
+    kn = torch.cat([synth.token_kv(geom, 50 + s, L)[0][L - q_lens[s]:] for s, L in enumerate(lengths)])
+    vn = torch.cat([synth.token_kv(geom, 50 + s, L)[1][L - q_lens[s]:] for s, L in enumerate(lengths)])
+    kc = nan_cache(cfg.k_cache_shape(plan.num_pages))
+    vc = nan_cache(cfg.v_cache_shape(plan.num_pages))
+    bi.bi_kv_write(cfg, kn.to(DEV), vn.to(DEV), torch.tensor(slots, device=DEV), kc, vc)
+    k0 = np.full((plan.num_pages, 16, 2, 64), np.nan)
+    v0 = k0.copy()
+    kr, vr = oracle.kv_write_ref(k0, v0, synth.to_f64(kn), synth.to_f64(vn), ref, 16)
+    np.testing.assert_array_equal(logical_k(kc), kr)   # NaN == NaN positionally
+    np.testing.assert_array_equal(logical_v(vc), vr)
+
+
+def test_slot_mapping_out_of_range_pages_give_minus_one():
+    pt = torch.tensor([[0, 7, -3]], dtype=torch.int32, device=DEV)
+    sl = torch.tensor([40], dtype=torch.int32, device=DEV)
+    qsl = torch.tensor([0, 40], dtype=torch.int32, device=DEV)
+    slots = bi.bi_slot_mapping(pt, sl, qsl, 40, 16, 5).cpu().numpy()
+    assert slots[:16].tolist() == list(range(16))
+    assert (slots[16:] == -1).all()
+
+
+# ---------------------------------------------------------------- a2 + a3: attention parity
+
+def _decode_case(geom, cfg, lengths, seed, order=None, stride_extra=0):
+    reqs = {i: Request(seed * 100 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, sum(synth.pages_needed(L, 16) for L in lengths) + 7, seed)
+    order = list(range(len(lengths))) if order is None else order
+    run_step(kv, reqs, [(i, lengths[i] - 1) for i in order], attention=False)
+    out = run_step(kv, reqs, [(i, 1) for i in order], stride_extra=stride_extra)
+    return reqs, out
+
+
+@pytest.mark.parametrize("S", [32, 256])
+def test_config1_tiny_decode_parity(S):
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=S)
+    lengths = [17, 33, 64, 100]
+    reqs, out = _decode_case(geom, cfg, lengths, seed=1, order=[2, 0, 3, 1])
+    ref = oracle_rows(reqs, list(out.keys()), geom, 0)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_prefill_chunks_parity_llama_shape(window):
+    geom = synth.Geometry(32, 8, 128, 16)
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256, window=window)
+    lengths = [300, 777, 1029]
+    reqs = {i: Request(900 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 200, seed=9)
+    run_step(kv, reqs, [(0, 250), (1, 700), (2, 900)], attention=False)
+    out = run_step(kv, reqs, [(0, 50), (1, 77), (2, 129)])
+    keys = [k for k in out if k[1] % 7 == 0 or k[1] == lengths[k[0]] - 1]
+    ref = oracle_rows(reqs, keys, geom, window)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+def test_gemma_shape_d256_window_parity():
+    geom = synth.Geometry(8, 4, 256, 16)
+    cfg = bi.AttnConfig(8, 4, 256, split_size=256, window=1024)
+    lengths = [1500, 2100, 40]
+    reqs = {i: Request(700 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 260, seed=4)
+    run_step(kv, reqs, [(0, 1499), (1, 2030), (2, 10)], attention=False)
+    out = run_step(kv, reqs, [(0, 1), (1, 70), (2, 30)])
+    keys = [k for k in out if k[1] % 5 == 0 or k[1] == lengths[k[0]] - 1]
+    ref = oracle_rows(reqs, keys, geom, 1024)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+def test_single_key_is_v0_bitwise():
+    geom = synth.Geometry(32, 8, 128, 16)
+    cfg = bi.AttnConfig(32, 8, 128)
+    reqs = {0: Request(5, 1, geom), 1: Request(6, 1, geom)}
+    kv = PagedKV(cfg, 8, seed=2)
+    out = run_step(kv, reqs, [(0, 1), (1, 1)])
+    for rid in (0, 1):
+        v0 = reqs[rid].v[0]                         # [H_kv, D] bf16
+        expect = v0.repeat_interleave(4, dim=0)     # head h reads KV head h // 4
+        assert torch.equal(out[(rid, 0)].view(torch.int16), expect.view(torch.int16))
+
+
+def test_split_phase_partials_parity():
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=32)
+    lengths, q_lens = [100, 70], [3, 20]
+    reqs = {i: Request(40 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 20, seed=8)
+    run_step(kv, reqs, [(0, lengths[0]), (1, lengths[1])], attention=False)
+    tabs = [kv.tables[0], kv.tables[1]]
+    pt = page_table_tensor(tabs, 8).to(DEV)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    qsl_h = np.array([0, 3, 23])
+    qsl = torch.tensor(qsl_h, dtype=torch.int32, device=DEV)
+    q = torch.cat([reqs[0].q[97:100], reqs[1].q[50:70]]).to(DEV)
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, 23, 100))
+    bi.bi_paged_attention_split(cfg, q, kv.k, kv.v, pt, sl, qsl, 100, ws)
+    ns = 4
+    ml, acc = bi.workspace_views(cfg, ws, 23, ns)
+    ml, acc = ml.cpu().double().numpy(), acc.cpu().double().numpy()
+    kc, vc = logical_k(kv.k), logical_v(kv.v)
+    pt_h = page_table_tensor(tabs, 8).numpy()
+    m, l, a, valid = oracle.split_partials_ref(synth.to_f64(q.cpu()), kc, vc, pt_h, lengths, qsl_h, 2, 16, 32)
+    R = 23 * 4
+    valid = valid.reshape(R, ns)
+    gm, gl, ga = ml[:, :, 0][valid], ml[:, :, 1][valid], acc[valid]
+    om, ol, oa = m.reshape(R, ns)[valid], l.reshape(R, ns)[valid], a.reshape(R, ns, 64)[valid]
+    assert np.max(np.abs(gm - om)) <= 1e-3 * max(1.0, np.max(np.abs(om)))
+    assert np.max(np.abs(gl / ol - 1)) <= 1e-2
+    assert np.max(np.abs(ga / gl[:, None] - oa / ol[:, None])) <= BF16_TOL
+
+
+def test_merge_phase_parity_on_synthetic_partials():
+    cfg = bi.AttnConfig(4, 2, 64, split_size=32)
+    T, H, D, L = 5, 4, 64, 130          # one sequence of 130 keys, 5 query rows -> 5 splits
+    ns = 5
+    rng = torch.Generator().manual_seed(77)
+    m = (torch.rand((T * H, ns), generator=rng) * 20 - 10).double()
+    l = (torch.rand((T * H, ns), generator=rng) * 30 + 1).double()
+    a = torch.randn((T * H, ns, D), generator=rng).double() * l[:, :, None]
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, T, L))
+    ml, acc = bi.workspace_views(cfg, ws, T, ns)
+    ml[:, :, 0] = m.float().to(DEV)
+    ml[:, :, 1] = l.float().to(DEV)
+    acc[:] = a.float().to(DEV)
+    sl = torch.tensor([L], dtype=torch.int32, device=DEV)
+    qsl = torch.tensor([0, T], dtype=torch.int32, device=DEV)
+    out = bi.bi_paged_attention_merge(cfg, sl, qsl, T, L, ws).cpu()
+    mf, lf, af = (x.float().double().numpy() for x in (m, l, a))
+    valid = np.ones((T, H, ns), dtype=bool)
+    ref = oracle.merge_ref(mf.reshape(T, H, ns), lf.reshape(T, H, ns), af.reshape(T, H, ns, D), valid)
+    assert np.max(np.abs(synth.to_f64(out) - ref)) <= BF16_TOL
+
+
+def test_full_size_llama_decode_sampled_parity():
+    """8B-shaped decode at B = 256 (the benchmarked launch), oracle on sampled sequences."""
+    from synth.workloads import build_decode_workload
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    wl = build_decode_workload(32, 8, 128, batch=256, seed=2000)
+    out = bi.bi_paged_attention(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                wl.max_seq_len)
+    torch.cuda.synchronize()
+    sample = [0, 17, 101, 255]
+    errs = []
+    for s in sample:
+        kk, vv, table, L = wl.host_sequence(s)
+        q = synth.to_f64(wl.q[s:s + 1].cpu())
+        ref = oracle.attention_ref(q, kk, vv, table, [L], [0, 1], 8, 16)
+        errs.append(float(np.max(np.abs(synth.to_f64(out[s:s + 1].cpu()) - ref))))
+    assert max(errs) <= BF16_TOL, errs
+
+
+# ---------------------------------------------------------------- a4: RMSNorm
+
+@pytest.mark.parametrize("M", [1, 7, 64])
+def test_rmsnorm_parity(M):
+    x = synth.normal_bf16((M, 4096), 401)
+    g = synth.normal_bf16((4096,), 402, std=0.1, mean=1.0)
+    y = bi.bi_rmsnorm(x.to(DEV), g.to(DEV), 1e-5).cpu()
+    ref = oracle.rmsnorm_ref(synth.to_f64(x), synth.to_f64(g), 1e-5)
+    assert np.max(np.abs(synth.to_f64(y) - ref)) <= BF16_TOL
+
+
+def test_rmsnorm_ragged_hidden_and_strides():
+    H = 2568                              # not a multiple of the 2048-element sweep of a workgroup
+    x = synth.normal_bf16((9, H + 8), 403)
+    g = synth.normal_bf16((H,), 404, std=0.1, mean=1.0)
+    xd = x.to(DEV)[:, :H]
+    out = torch.zeros((9, H + 16), dtype=torch.bfloat16, device=DEV)
+    bi.bi_rmsnorm(xd, g.to(DEV), 1e-6, out=out[:, :H])
+    ref = oracle.rmsnorm_ref(synth.to_f64(x[:, :H]), synth.to_f64(g), 1e-6)
+    assert np.max(np.abs(synth.to_f64(out[:, :H].cpu()) - ref)) <= BF16_TOL
+    assert (out[:, H:].float() == 0).all()
+
+
+# ---------------------------------------------------------------- a5: GEMM
+
+def test_gemm_small_integers_exact_fp32():
+    a = synth.small_int_bf16((37, 4096), 501)
+    w = synth.small_int_bf16((300, 4096), 502)
+    c = bi.bi_gemm(a.to(DEV), w.to(DEV), out_dtype=torch.float32).cpu()
+    ref = oracle.gemm_ref(synth.to_f64(a), synth.to_f64(w))
+    assert np.array_equal(c.double().numpy(), ref)
+
+
+@pytest.mark.parametrize("M,N", [(1, 14336), (7, 1000), (64, 2048), (300, 777)])
+def test_gemm_parity(M, N):
+    a = synth.normal_bf16((M, 4096), 511)
+    w = synth.normal_bf16((N, 4096), 512, std=0.02)
+    ad, wd = a.to(DEV), w.to(DEV)
+    c32 = bi.bi_gemm(ad, wd, out_dtype=torch.float32).cpu().double().numpy()
+    c16 = synth.to_f64(bi.bi_gemm(ad, wd).cpu())
+    ref = oracle.gemm_ref(synth.to_f64(a), synth.to_f64(w))
+    bound = oracle.gemm_abs_ref(synth.to_f64(a), synth.to_f64(w))
+    assert np.all(np.abs(c32 - ref) <= 1e-3 * bound)
+    assert np.max(np.abs(c16 - ref)) <= BF16_TOL
+
+
+def test_gemm_lm_head_full_size_sampled():
+    """M = 1024 x N = 128256 x K = 4096 with fp32 logits; oracle on sampled entries."""
+    M, N, K = 1024, 128256, 4096
+    a = synth.normal_bf16_device((M, K), 521)
+    w = synth.normal_bf16_device((N, K), 522, std=0.02)
+    c = bi.bi_gemm(a, w, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    rows = torch.tensor([0, 1, 511, 1023])
+    cols = torch.tensor([0, 5, 77777, 128255, 64000, 12345])
+    ah = synth.to_f64(a[rows].cpu())
+    wh = synth.to_f64(w[cols].cpu())
+    ref = oracle.gemm_ref(ah, wh)
+    got = c[rows][:, cols].cpu().double().numpy()
+    assert np.all(np.abs(got - ref) <= 1e-3 * oracle.gemm_abs_ref(ah, wh))
