@@ -23,6 +23,12 @@ if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first with "
                       "`python -m deterministic_paged_attention_amd.build` (or __graft_entry__.build())")
 
+# torch is imported first so that its HIP runtime is the one loaded into the
+# process: libbi.so then binds to that same libamdhip64 (same soname) instead of
+# bringing a second runtime in from the system ROCm install.  One process, one
+# HIP runtime, shared with the tensors and streams torch hands us.
+import torch as _torch_runtime  # noqa: E402,F401
+
 lib = ctypes.CDLL(LIB_PATH)
 
 c_i32, c_i64, c_f32, c_sz, c_vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_float, ctypes.c_size_t, ctypes.c_void_p

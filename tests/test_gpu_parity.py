@@ -33,7 +33,7 @@ def test_slot_mapping_and_kv_write_bit_exact():
     lengths, q_lens = [17, 33, 64, 100], [17, 5, 1, 37]
     plan = synth.random_page_plan(lengths, 16, seed=3, slack=5)
     pt_host = plan.table(stride=9).numpy()
-    pt_host[2, 3] = 999  # an entry beyond what sequence 2 uses: never read
+    pt_host[2, 6] = 999  # an entry beyond the 4 pages sequence 2 uses: never read
     pt = torch.tensor(pt_host, device=DEV)
     sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
     qsl_h = np.concatenate([[0], np.cumsum(q_lens)])
@@ -171,7 +171,10 @@ def test_merge_phase_parity_on_synthetic_partials():
     qsl = torch.tensor([0, T], dtype=torch.int32, device=DEV)
     out = bi.bi_paged_attention_merge(cfg, sl, qsl, T, L, ws).cpu()
     mf, lf, af = (x.float().double().numpy() for x in (m, l, a))
-    valid = np.ones((T, H, ns), dtype=bool)
+    # row t sits at p = L - T + t and reads the splits 0 .. p // 32 only
+    valid = np.zeros((T, H, ns), dtype=bool)
+    for t in range(T):
+        valid[t, :, : (L - T + t) // 32 + 1] = True
     ref = oracle.merge_ref(mf.reshape(T, H, ns), lf.reshape(T, H, ns), af.reshape(T, H, ns, D), valid)
     assert np.max(np.abs(synth.to_f64(out) - ref)) <= BF16_TOL
 
