@@ -149,7 +149,7 @@ def main():
     slots = torch.empty(B, dtype=torch.int32, device=dev)
     attn = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
     y = torch.empty((B, HIDDEN), dtype=torch.bfloat16, device=dev)
-    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, wl.max_seq_len))
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, B, wl.max_seq_len))
     stream = torch.cuda.current_stream()
 
     names = ["rmsnorm", "gemm_qkv", "slot_mapping", "kv_write", "attn_split", "attn_merge", "gemm_o"]
@@ -201,7 +201,7 @@ def main():
     if not args.no_splitk:
         props = torch.cuda.get_device_properties(0)
         nsplit = bi.bi_splitk_attention_heuristic(cfg, B, wl.max_seq_len, props.multi_processor_count, 8)
-        ws_k = bi.alloc_workspace(bi.bi_paged_attention_splitk_workspace_size(cfg, B, wl.max_seq_len, nsplit))
+        ws_k = bi.alloc_workspace(bi.bi_paged_attention_splitk_workspace_size(cfg, B, B, wl.max_seq_len, nsplit))
         out_k = torch.empty_like(attn)
 
         def run_inv():

@@ -65,7 +65,7 @@ _sig("bi_attn_config_query", c_i32, c_vp, ctypes.POINTER(bi_attn_desc), P_i32)
 _sig("bi_kv_cache_bytes", c_i32, c_vp, c_i64, ctypes.POINTER(c_sz))
 _sig("bi_slot_mapping", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp)
 _sig("bi_kv_write", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp)
-_sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, ctypes.POINTER(c_sz))
+_sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
@@ -75,7 +75,7 @@ _sig("bi_gemm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i6
 _sig("bi_check_page_table", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_check_write_plan", c_i32, c_vp, c_i32, c_vp, c_i32, c_i32)
 _sig("bi_splitk_attention_heuristic", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, P_i32)
-_sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
+_sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_splitk", c_i32, *_ATTN_ARGS, c_i32, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_gemm_splitk_heuristic", c_i32, c_i64)
 _sig("bi_gemm_splitk_workspace_size", c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_sz))
@@ -198,15 +198,16 @@ def bi_kv_write(cfg: AttnConfig, k_new, v_new, slot_mapping, k_cache, v_cache, s
                            _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(stream)))
 
 
-def bi_paged_attention_workspace_size(cfg: AttnConfig, num_tokens: int, max_seq_len: int) -> int:
+def bi_paged_attention_workspace_size(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int) -> int:
     b = c_sz()
-    _check(lib.bi_paged_attention_workspace_size(cfg.handle, num_tokens, max_seq_len, ctypes.byref(b)))
+    _check(lib.bi_paged_attention_workspace_size(cfg.handle, num_seqs, num_tokens, max_seq_len, ctypes.byref(b)))
     return b.value
 
 
-def bi_paged_attention_splitk_workspace_size(cfg: AttnConfig, num_tokens: int, max_seq_len: int, num_splits: int):
+def bi_paged_attention_splitk_workspace_size(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int,
+                                             num_splits: int):
     b = c_sz()
-    _check(lib.bi_paged_attention_splitk_workspace_size(cfg.handle, num_tokens, max_seq_len, num_splits,
+    _check(lib.bi_paged_attention_splitk_workspace_size(cfg.handle, num_seqs, num_tokens, max_seq_len, num_splits,
                                                         ctypes.byref(b)))
     return b.value
 
@@ -237,7 +238,8 @@ def bi_paged_attention(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_len
     args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
     T = q.shape[0]
     if workspace is None:
-        workspace = alloc_workspace(bi_paged_attention_workspace_size(cfg, T, max_seq_len), q.device)
+        workspace = alloc_workspace(bi_paged_attention_workspace_size(cfg, seq_lens.shape[0], T, max_seq_len),
+                                    q.device)
     if out is None:
         out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
     _check(lib.bi_paged_attention(*args, max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
@@ -288,8 +290,8 @@ def bi_paged_attention_splitk(cfg: AttnConfig, q, k_cache, v_cache, page_table, 
     args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
     T = q.shape[0]
     if workspace is None:
-        workspace = alloc_workspace(bi_paged_attention_splitk_workspace_size(cfg, T, max_seq_len, num_splits),
-                                    q.device)
+        workspace = alloc_workspace(bi_paged_attention_splitk_workspace_size(cfg, seq_lens.shape[0], T, max_seq_len,
+                                                                             num_splits), q.device)
     if out is None:
         out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
     _check(lib.bi_paged_attention_splitk(*args, max_seq_len, num_splits, _ptr(workspace),

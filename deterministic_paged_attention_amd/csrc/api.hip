@@ -58,14 +58,16 @@ constexpr size_t kAlign = 256;
 size_t round_up(size_t x, size_t a) { return (x + a - 1) / a * a; }
 
 struct WsLayout {
-  size_t ml_bytes = 0, acc_offset = 0, total = 0;
+  size_t ml_bytes = 0, acc_offset = 0, plan_offset = 0, total = 0;
 };
 
-WsLayout ws_layout(int head_dim, int64_t rows, int64_t ns) {
+// ml float2 [R][ns] | pad to 256 | acc float [R][ns][D] | pad to 256 | plan int32 [num_seqs + 1]
+WsLayout ws_layout(int head_dim, int64_t rows, int64_t ns, int64_t num_seqs) {
   WsLayout w;
   w.ml_bytes = (size_t)rows * (size_t)ns * sizeof(float) * 2;
   w.acc_offset = round_up(w.ml_bytes, kAlign);
-  w.total = w.acc_offset + (size_t)rows * (size_t)ns * (size_t)head_dim * sizeof(float);
+  w.plan_offset = round_up(w.acc_offset + (size_t)rows * (size_t)ns * (size_t)head_dim * sizeof(float), kAlign);
+  w.total = w.plan_offset + (size_t)(num_seqs + 1) * sizeof(int32_t);
   return w;
 }
 
@@ -224,22 +226,22 @@ bi_status bi_kv_write(const bi_attn_config* cfg, const void* k_new_dev, int64_t 
                     "kv_write launch");
 }
 
-bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_tokens, int32_t max_seq_len,
-                                            size_t* bytes) {
+bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                            int32_t max_seq_len, size_t* bytes) {
   if (bi_status st = check_cfg(cfg)) return st;
-  if (!bytes || num_tokens < 0 || max_seq_len < 1)
-    return fail(BI_ERR_INVALID_ARG, "bytes NULL, num_tokens < 0 or max_seq_len < 1");
+  if (!bytes || num_seqs < 1 || num_tokens < 0 || max_seq_len < 1)
+    return fail(BI_ERR_INVALID_ARG, "bytes NULL, num_seqs < 1, num_tokens < 0 or max_seq_len < 1");
   const int64_t ns = (max_seq_len + (int64_t)cfg->desc.split_size - 1) / cfg->desc.split_size;
-  *bytes = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, ns).total;
+  *bytes = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, ns, num_seqs).total;
   return ok();
 }
 
-bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_tokens,
+bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                                    int32_t max_seq_len, int32_t num_splits, size_t* bytes) {
   if (bi_status st = check_cfg(cfg)) return st;
-  if (!bytes || num_tokens < 0 || max_seq_len < 1 || num_splits < 1)
-    return fail(BI_ERR_INVALID_ARG, "bytes NULL, num_tokens < 0, max_seq_len < 1 or num_splits < 1");
-  *bytes = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, num_splits).total;
+  if (!bytes || num_seqs < 1 || num_tokens < 0 || max_seq_len < 1 || num_splits < 1)
+    return fail(BI_ERR_INVALID_ARG, "bytes NULL, num_seqs < 1, num_tokens < 0, max_seq_len < 1 or num_splits < 1");
+  *bytes = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, num_splits, num_seqs).total;
   return ok();
 }
 
@@ -249,13 +251,16 @@ namespace {
 
 bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split, int32_t ns, void* ws, size_t ws_bytes,
                     hipStream_t stream) {
-  const WsLayout L = ws_layout(cfg->desc.head_dim, (int64_t)c.num_tokens * cfg->desc.num_q_heads, ns);
+  const WsLayout L = ws_layout(cfg->desc.head_dim, (int64_t)c.num_tokens * cfg->desc.num_q_heads, ns, c.num_seqs);
   if (!ws && L.total) return fail(BI_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < L.total)
     return fail(BI_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, L.total);
   if (!aligned(ws, 16)) return fail(BI_ERR_INVALID_ARG, "workspace must be 16-byte aligned");
   if (c.num_tokens == 0) return ok();
-  if ((ns + bi::kSplitWaves - 1) / bi::kSplitWaves > 65535) return fail(BI_ERR_OUT_OF_RANGE, "too many splits");
+  // Work items are counted in 32-bit integers: bound their number.
+  const int64_t tq = 16 >> cfg->log2_group;
+  if (((int64_t)c.num_tokens / tq + c.num_seqs) * cfg->desc.num_kv_heads * ns > 0x7fffffffLL)
+    return fail(BI_ERR_OUT_OF_RANGE, "too many work items");
   if ((int64_t)c.num_tokens * cfg->desc.num_q_heads * ns > 0x7fffffffffffLL)
     return fail(BI_ERR_OUT_OF_RANGE, "workspace index overflow");
   bi::AttnSplitArgs a;
@@ -279,13 +284,14 @@ bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split,
   a.qk_scale_log2 = cfg->qk_scale_log2;
   a.ws_ml = (float2*)ws;
   a.ws_acc = (float*)((char*)ws + L.acc_offset);
+  a.plan = (int32_t*)((char*)ws + L.plan_offset);
   return hip_status(bi::launch_attn_split(cfg->desc.head_dim, a, stream), "attention split launch");
 }
 
 bi_status run_merge(const bi_attn_config* cfg, const int32_t* seq_lens, const int32_t* qsl, int32_t num_seqs,
                     int32_t num_tokens, int32_t split, int32_t ns, const void* ws, size_t ws_bytes, void* out,
                     hipStream_t stream) {
-  const WsLayout L = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, ns);
+  const WsLayout L = ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, ns, num_seqs);
   if (!ws && L.total) return fail(BI_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < L.total)
     return fail(BI_ERR_WORKSPACE_TOO_SMALL, "workspace %zu bytes < required %zu", ws_bytes, L.total);

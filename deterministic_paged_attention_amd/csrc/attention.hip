@@ -51,14 +51,30 @@ __device__ __forceinline__ f32x4 mfma16x16x32(const bf16x8& a, const bf16x8& b, 
 
 __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2f(x); }
 
-// Largest s with start(s) <= x, start(s) = qsl[s] / tq + s (monotone in s).
-__device__ __forceinline__ int find_block_seq(const int32_t* qsl, int num_seqs, int tq, int x) {
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] / tq + mid <= x) lo = mid; else hi = mid - 1;
-  }
-  return lo;
+// Read of a table the split kernel never writes (page table, sequence
+// metadata, work plan) through the constant address space: the compiler then
+// keeps uniform reads on the scalar unit, whose waits do not touch the vector
+// memory counter that tracks the K/V tiles in flight.
+typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
+__device__ __forceinline__ int ldc(const int32_t* p, int64_t i) { return ((const_i32_ptr)p)[i]; }
+
+// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query row,
+// with the gfx950 lane-swap instructions (VALU only; no LDS traffic and no
+// wait on the memory counters).  Swapping a value with itself and combining
+// the two results gives every lane of a row the same operands in the same
+// order: (r0 op r1) op (r2 op r3), where ri is the value of lane group i.
+__device__ __forceinline__ float row4_max(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
+}
+
+__device__ __forceinline__ float row4_sum(float v) {
+  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Largest s with qsl[s] <= t.
@@ -72,180 +88,374 @@ __device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, 
 }
 
 // ---------------------------------------------------------------------------
-// Split phase.  Grid: x = query-row block (global numbering qsl[s]/Tq + s + b),
-// y = KV head, z = group of kSplitWaves splits; one wave per split.
+// Building blocks of the split phase.
+// ---------------------------------------------------------------------------
+
+// Online-softmax state of the query row held by this lane (the four lanes of a
+// row hold identical m and l).
+template <int D>
+struct SplitState {
+  float m, l;
+  f32x4 acc[D / 16];
+  __device__ __forceinline__ void init() {
+    m = -INFINITY;
+    l = 0.f;
+#pragma unroll
+    for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
+  }
+};
+
+// Operands of one 32-key tile (two pages of 16 keys) for this lane.
+template <int D>
+struct TileData {
+  u32x4 kf[2][D / 32];   // K rows: A operand of S^T = K Q^T
+  u32x2 vf[2][D / 16];   // V^T fragments: A operand of O^T = V^T P^T
+  u32x2 vmask[2];        // per page: keeps the bits of this lane's keys below k_len
+};
+
+// Keys [lo, hi] of this split visible to this lane's row (empty if lo > hi).
+struct RowMask {
+  int lo, hi;
+};
+
+// Page-table entries of the two 16-key halves of a tile.  The read is
+// unconditional (its index is clamped to the last entry the sequence uses, so
+// entries past ceil(k_len / 16) are never read) and its result is first needed
+// by the next stage, so the scalar load latency hides behind a tile compute.
+__device__ __forceinline__ int2 tile_pages(const int32_t* pt_row, int last_entry, int tile) {
+  return make_int2(ldc(pt_row, min(2 * tile, last_entry)), ldc(pt_row, min(2 * tile + 1, last_entry)));
+}
+
+// Cache policy of the K/V tile loads: non-temporal (each byte is read once).
+constexpr int kStreamLoad = 2;
+
+// Raw buffer resource over one page of one KV head (gfx9 word 3: 32-bit data
+// format, no swizzle).  With num_records = 0 every load through it returns
+// zero without touching memory.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* base, int bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, bytes, 0x00020000);
+}
+
+// Issue the loads of one tile.  Every call issues the same loads (pages past
+// k_len, past the page-table row or past the split go through an empty buffer
+// resource and read as zero), so the number of loads in flight is static and
+// the wait before a tile is computed covers only that tile's loads.  Nothing
+// here reads the loaded registers.  K rows of keys at or past k_len need no
+// clearing: a key's row of S^T only feeds that key's scores, which the mask
+// replaces by -inf.  V of such keys must be zero (0 * NaN would reach every
+// row through the PV contraction; never-written slots may hold NaN), so a
+// per-page bit mask is recorded and applied when the tile is computed.
+template <int D>
+__device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k_len, int tile, int tile_end,
+                                          int2 pid, int lane, TileData<D>& t) {
+  constexpr int NSTEP = D / 32;
+  constexpr int NBLK = D / 16;
+  constexpr int PAGE_BYTES = D * 16 * 2;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int64_t head_elems = (int64_t)D * 16;
+  const bool live_tile = tile < tile_end;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    // A half is read only if it lies in the split, below k_len, inside the
+    // page-table row, and names a page of the pool.
+    const int entry = 2 * tile + b;
+    const int raw = b == 0 ? pid.x : pid.y;
+    const int pgc = min(max(raw, 0), a.num_pages - 1);  // always a page of the pool
+    const bool ok = live_tile && entry * 16 < k_len && entry < a.pt_stride && raw == pgc;
+    const int pg = ok ? pgc : -1;
+    const int nl = min(16, k_len - (tile * 32 + 16 * b)) - 4 * g4;  // valid keys among this lane's four
+    t.vmask[b].x = (pg < 0) ? 0u : (nl >= 2 ? 0xffffffffu : (nl == 1 ? 0x0000ffffu : 0u));
+    t.vmask[b].y = (pg < 0) ? 0u : (nl >= 4 ? 0xffffffffu : (nl == 3 ? 0x0000ffffu : 0u));
+    const int64_t base = ((int64_t)pgc * a.num_kv_heads + kvh) * head_elems;
+    const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + base, pg < 0 ? 0 : PAGE_BYTES);
+    const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + base, pg < 0 ? 0 : PAGE_BYTES);
+#pragma unroll
+    for (int st = 0; st < NSTEP; ++st)
+      t.kf[b][st] = __builtin_amdgcn_raw_buffer_load_b128(kr, (64 * st + lane) * 16, 0, kStreamLoad);
+#pragma unroll
+    for (int n = 0; n < NBLK; ++n)
+      t.vf[b][n] = __builtin_amdgcn_raw_buffer_load_b64(vr, (256 * n + 16 * r + 4 * g4) * 2, 0, kStreamLoad);
+  }
+}
+
+// One online-softmax step over a 32-key tile for this lane's row.  A row with
+// no visible key in the tile keeps (m, l, acc) bit-for-bit (select, not update).
+template <int D>
+__device__ __forceinline__ void compute_tile(SplitState<D>& st, const TileData<D>& t, const bf16x8* qf, int tile,
+                                             const RowMask& rm, int g4, float qk_scale_log2) {
+  constexpr int NSTEP = D / 32;
+  constexpr int NBLK = D / 16;
+  const int kb = tile << 5;
+  // Scores: lane holds keys kb + 16b + 4*g4 + i (i = 0..3) of its row.
+  float x[2][4];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < NSTEP; ++s) sc = mfma16x16x32(__builtin_bit_cast(bf16x8, t.kf[b][s]), qf[s], sc);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int key = kb + 16 * b + 4 * g4 + i;
+      const bool ok = key >= rm.lo && key <= rm.hi;
+      x[b][i] = ok ? sc[i] * qk_scale_log2 : -INFINITY;
+    }
+  }
+  float tmax = x[0][0];
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[b][i]);
+  tmax = row4_max(tmax);
+  const bool live = tmax != -INFINITY;  // this row sees at least one key here
+
+  const float m_new = fmaxf(st.m, tmax);
+  const float alpha = (st.m == -INFINITY) ? 0.f : exp2_hw(st.m - m_new);
+  __bf16 pb[2][4];
+  float rs = 0.f;
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const float e = (x[b][i] != -INFINITY) ? exp2_hw(x[b][i] - m_new) : 0.f;
+      pb[b][i] = (__bf16)e;
+      rs += (float)pb[b][i];
+    }
+  rs = row4_sum(rs);
+  const float l_new = __builtin_fmaf(alpha, st.l, rs);
+
+  const bf16x8 pfrag = {pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
+#pragma unroll
+  for (int n = 0; n < NBLK; ++n) {
+    const u32x4 vv = {t.vf[0][n].x & t.vmask[0].x, t.vf[0][n].y & t.vmask[0].y, t.vf[1][n].x & t.vmask[1].x,
+                      t.vf[1][n].y & t.vmask[1].y};
+    const f32x4 cin = st.acc[n] * alpha;
+    const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag, cin);
+    st.acc[n] = live ? res : st.acc[n];
+  }
+  st.m = live ? m_new : st.m;
+  st.l = live ? l_new : st.l;
+}
+
+// ---------------------------------------------------------------------------
+// Work list.  An item is one (sequence, query-row block, KV head, split).  The
+// plan kernel writes, for every sequence, the index of its first item
+// (an exclusive prefix sum of integer counts, so exact whatever the order);
+// item u of sequence s has local index l = u - first[s], with the split
+// fastest: split = lo_split(s) + l % nsplit(s), then KV head, then row block.
+// A row block whose rows see no key of a split still owns that item; it is
+// processed as one fully masked tile and writes nothing.
+// ---------------------------------------------------------------------------
+struct SeqSplits {
+  int lo, n;  // first split meeting any row of the sequence, number of splits
+};
+
+__device__ __forceinline__ SeqSplits seq_splits(int q_len, int k_len, int window, int S) {
+  SeqSplits r{0, 0};
+  if (q_len <= 0 || k_len <= 0 || q_len > k_len) return r;
+  const int p_first = k_len - q_len;
+  const int lo = window > 0 ? max(0, p_first - window + 1) : 0;
+  r.lo = lo / S;
+  r.n = (k_len - 1) / S - r.lo + 1;
+  return r;
+}
+
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) {
+  __shared__ int wave_tot[16];
+  __shared__ int carry_sh;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wv = tid >> 6;
+  const int tq = kRowsPerBlock >> a.log2_group;
+  if (tid == 0) carry_sh = 0;
+  __syncthreads();
+  for (int base = 0; base < a.num_seqs; base += 1024) {
+    const int s = base + tid;
+    int c = 0;
+    if (s < a.num_seqs) {
+      const int q_len = a.qsl[s + 1] - a.qsl[s];
+      const SeqSplits sp = seq_splits(q_len, a.seq_lens[s], a.window, a.split);
+      c = sp.n > 0 ? ((q_len + tq - 1) / tq) * a.num_kv_heads * sp.n : 0;
+    }
+    int incl = c;  // inclusive scan within the wave
+#pragma unroll
+    for (int off = 1; off < 64; off <<= 1) {
+      const int v = __shfl_up(incl, off);
+      if (lane >= off) incl += v;
+    }
+    if (lane == 63) wave_tot[wv] = incl;
+    __syncthreads();
+    int before = carry_sh;
+    for (int w = 0; w < wv; ++w) before += wave_tot[w];
+    if (s < a.num_seqs) a.plan[s] = before + incl - c;
+    __syncthreads();
+    if (tid == 1023) carry_sh = before + incl;
+    __syncthreads();
+  }
+  if (tid == 0) a.plan[a.num_seqs] = carry_sh;
+}
+
+// Wave-uniform description of one item.
+struct Item {
+  int valid;                 // 0: past the end of the work list
+  int s, kvh, sigma, q0, tq0, nrow_tok, k_len, p_first;
+  int tile_begin, tile_end;  // at least one tile
+  int last_entry;            // last page-table entry the sequence uses
+  const int32_t* pt_row;
+};
+
+__device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, int u, int total) {
+  Item it;
+  it.valid = u < total;
+  it.s = 0; it.kvh = 0; it.sigma = 0; it.q0 = 0; it.tq0 = 0; it.nrow_tok = 0; it.k_len = 0; it.p_first = 0;
+  it.tile_begin = 0; it.tile_end = 1; it.last_entry = 0; it.pt_row = a.page_table;
+  if (!it.valid) return it;
+  int lo = 0, hi = a.num_seqs - 1;  // largest s with plan[s] <= u
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (ldc(a.plan, mid) <= u) lo = mid; else hi = mid - 1;
+  }
+  const int s = lo;
+  const int local = u - ldc(a.plan, s);
+  const int q0 = ldc(a.qsl, s);
+  const int q_len = ldc(a.qsl, s + 1) - q0;
+  const int k_len = ldc(a.seq_lens, s);
+  const SeqSplits sp = seq_splits(q_len, k_len, a.window, a.split);
+  const int tq = kRowsPerBlock >> a.log2_group;
+  const int sigma = sp.lo + local % sp.n;
+  const int rest = local / sp.n;
+  it.s = s;
+  it.kvh = rest % a.num_kv_heads;
+  it.sigma = sigma;
+  it.q0 = q0;
+  it.tq0 = (rest / a.num_kv_heads) * tq;
+  it.nrow_tok = min(tq, q_len - it.tq0);
+  it.k_len = k_len;
+  it.p_first = k_len - q_len + it.tq0;
+  const int p_last = it.p_first + it.nrow_tok - 1;
+  const int lo_first = a.window > 0 ? max(0, it.p_first - a.window + 1) : 0;
+  const int key_begin = max(sigma * a.split, lo_first);
+  const int key_end = min(sigma * a.split + a.split, p_last + 1);
+  it.tile_begin = key_begin < key_end ? (key_begin >> 5) : (sigma * a.split) >> 5;
+  it.tile_end = key_begin < key_end ? ((key_end + 31) >> 5) : it.tile_begin + 1;
+  it.last_entry = max(0, min((k_len + 15) / 16, a.pt_stride) - 1);
+  it.pt_row = a.page_table + (int64_t)s * a.pt_stride;
+  return it;
+}
+
+// Per-lane part of an item: this lane's query row (token t of the block, head
+// hh of the GQA group), its visible keys inside the split, and its Q fragment
+// (B operand of S^T = K Q^T: step st, lane group g4 holds head-dim chunk
+// 4*st + g4).
+template <int D>
+struct ItemLane {
+  RowMask rm;
+  bf16x8 q[D / 32];
+};
+
+template <int D>
+__device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const Item& it, int lane) {
+  constexpr int NSTEP = D / 32;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int t = r >> a.log2_group;
+  const int hh = r & ((1 << a.log2_group) - 1);
+  const bool row_ok = it.valid && (t < it.nrow_tok) && (it.q0 + it.tq0 + t < a.num_tokens);
+  const int p = it.p_first + t;
+  ItemLane<D> L;
+  const int split_lo = it.sigma * a.split;
+  L.rm.lo = max(a.window > 0 ? max(0, p - a.window + 1) : 0, split_lo);
+  L.rm.hi = min(p, split_lo + a.split - 1);
+  if (!row_ok || p < 0) { L.rm.lo = 1; L.rm.hi = 0; }
+  // Rows past the block (padding columns of the MFMA) read the block's first
+  // row instead: their mask is empty, so their scores never reach any result
+  // (each MFMA output column depends only on its own Q column).
+  const int tok = min(it.q0 + it.tq0 + (row_ok ? t : 0), max(a.num_tokens - 1, 0));
+  const uint16_t* qrow = a.q + (int64_t)tok * a.q_stride + (int64_t)((it.kvh << a.log2_group) + hh) * D;
+#pragma unroll
+  for (int st = 0; st < NSTEP; ++st)
+    L.q[st] = __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(qrow + (4 * st + g4) * 8));
+  return L;
+}
+
+template <int D>
+__device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item& it, const ItemLane<D>& L,
+                                              const SplitState<D>& st, int lane) {
+  if (L.rm.lo > L.rm.hi) return;
+  const int r = lane & 15, g4 = lane >> 4;
+  const int t = r >> a.log2_group;
+  const int hh = r & ((1 << a.log2_group) - 1);
+  const int64_t row = (int64_t)(it.q0 + it.tq0 + t) * a.num_q_heads + (it.kvh << a.log2_group) + hh;
+  const int64_t idx = row * a.ns + it.sigma;
+  if (g4 == 0) a.ws_ml[idx] = make_float2(st.m, st.l);
+  float* ap = a.ws_acc + idx * D;
+#pragma unroll
+  for (int n = 0; n < D / 16; ++n) *reinterpret_cast<f32x4*>(ap + 16 * n + 4 * g4) = st.acc[n];
+}
+
+// ---------------------------------------------------------------------------
+// Split phase, persistent: the grid holds as many waves as the GPU keeps
+// resident; wave w processes items w, w + W, w + 2W, ...  Tiles stream through
+// two register buffers: while tile k is computed, tile k+1 is loading, and
+// tile k+1 may already belong to the wave's next item (whose description is
+// decoded while the current item is computed).  Which wave
+// computes an item, and when, has no effect on its arithmetic.
 // ---------------------------------------------------------------------------
 template <int D>
+struct SplitWave {
+  const AttnSplitArgs& a;
+  int lane, g4, total, stride, u;
+  Item cur, nxt;
+  ItemLane<D> curL;
+  SplitState<D> st;
+  int ct;  // tile of `cur` being computed
+
+  // Compute tile `ct` of `cur` from Bc while the next tile of the stream loads
+  // into Bl.  Returns false once the wave has no item left.
+  __device__ __forceinline__ bool step(TileData<D>& Bc, TileData<D>& Bl) {
+    const bool in_cur = ct + 1 < cur.tile_end;
+    const Item& L = in_cur ? cur : nxt;
+    const int lt = in_cur ? ct + 1 : nxt.tile_begin;
+    const int lend = (in_cur || nxt.valid) ? L.tile_end : lt;  // dead load past the last item
+    load_tile(a, L.kvh, L.k_len, lt, lend, tile_pages(L.pt_row, L.last_entry, lt), lane, Bl);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile(st, Bc, curL.q, ct, curL.rm, g4, a.qk_scale_log2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (in_cur) {
+      ++ct;
+      return true;
+    }
+    write_partial(a, cur, curL, st, lane);
+    st.init();
+    if (!nxt.valid) return false;
+    cur = nxt;
+    curL = item_lane<D>(a, cur, lane);  // Q loads overlap the tile loads already in flight
+    u += stride;
+    ct = cur.tile_begin;
+    nxt = decode_item(a, u + stride, total);
+    return true;
+  }
+};
+
+template <int D>
 __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const AttnSplitArgs a) {
-  constexpr int NSTEP = D / 32;  // 32-wide head-dim steps of QK^T
-  constexpr int NBLK = D / 16;   // 16-row head-dim blocks of O^T
   const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;       // MFMA column = query row of the block
-  const int g4 = lane >> 4;      // lane group = k-slot group of the MFMA operands
-  const int kvh = blockIdx.y;
-  const int sigma = blockIdx.z * kSplitWaves + wave;
-  if (sigma >= a.ns) return;
-
-  const int G = 1 << a.log2_group;
-  const int tq = kRowsPerBlock >> a.log2_group;  // tokens per row block
-  const int xb = blockIdx.x;
-  const int s = find_block_seq(a.qsl, a.num_seqs, tq, xb);
-  const int q0 = a.qsl[s];
-  const int q_len = a.qsl[s + 1] - q0;
-  const int k_len = a.seq_lens[s];
-  const int local = xb - (q0 / tq + s);
-  const int tq0 = local * tq;
-  if (local < 0 || tq0 >= q_len) return;
-
-  const int nrow_tok = min(tq, q_len - tq0);
-  const int p_first = k_len - q_len + tq0;
-  const int p_last = p_first + nrow_tok - 1;
-  if (p_last < 0) return;
-  const int lo_first = a.window > 0 ? max(0, p_first - a.window + 1) : 0;
-  const int S = a.split;
-  if (sigma < max(lo_first, 0) / S || sigma > p_last / S) return;
-  const int split_lo = sigma * S;
-  const int key_begin = max(split_lo, max(lo_first, 0));
-  const int key_end = min(split_lo + S, p_last + 1);  // exclusive
-  const int tile_begin = key_begin >> 5;
-  const int tile_end = (key_end + 31) >> 5;
-
-  // This lane's query row: token t of the block, head hh of the GQA group.
-  const int t = r >> a.log2_group;
-  const int hh = r & (G - 1);
-  const bool row_ok = (t < nrow_tok) && (q0 + tq0 + t < a.num_tokens);
-  const int p = p_first + t;
-  int rk_lo = max(a.window > 0 ? max(0, p - a.window + 1) : 0, split_lo);
-  int rk_hi = min(p, split_lo + S - 1);
-  if (!row_ok || p < 0) { rk_lo = 1; rk_hi = 0; }
-
-  // Q fragment (B operand of S^T = K Q^T): step st, lane group g4 holds the
-  // head-dim chunk 4*st + g4 (8 elements) of this lane's row.
-  bf16x8 qf[NSTEP];
-  {
-    const int tok = q0 + tq0 + (row_ok ? t : 0);
-    const uint16_t* qrow = a.q + (int64_t)tok * a.q_stride + (int64_t)((kvh << a.log2_group) + hh) * D;
-#pragma unroll
-    for (int st = 0; st < NSTEP; ++st) {
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (row_ok) v = *reinterpret_cast<const u32x4*>(qrow + (4 * st + g4) * 8);
-      qf[st] = __builtin_bit_cast(bf16x8, v);
-    }
-  }
-
-  float m_run = -INFINITY;
-  float l_run = 0.f;
-  f32x4 acc[NBLK];
-#pragma unroll
-  for (int n = 0; n < NBLK; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-  const int32_t* pt_row = a.page_table + (int64_t)s * a.pt_stride;
-  const int64_t head_elems = (int64_t)D * 16;  // one page of one KV head
-
-  for (int tile = tile_begin; tile < tile_end; ++tile) {
-    const int kb = tile << 5;
-    u32x4 kf[2][NSTEP];
-    u32x2 vf[2][NBLK];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      const int key0 = kb + 16 * b;
-      const int nvalid = min(16, k_len - key0);  // keys of this page below k_len
-      const int lp = key0 >> 4;
-      int pg = -1;
-      if (nvalid > 0 && lp < a.pt_stride) {
-        pg = pt_row[lp];
-        if (pg < 0 || pg >= a.num_pages) pg = -1;
-      }
-      if (pg >= 0) {
-        const int64_t base = ((int64_t)pg * a.num_kv_heads + kvh) * head_elems;
-        const uint16_t* kp = a.k_cache + base;
-        const uint16_t* vp = a.v_cache + base;
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st)
-          kf[b][st] = *reinterpret_cast<const u32x4*>(kp + (64 * st + lane) * 8);
-#pragma unroll
-        for (int n = 0; n < NBLK; ++n)
-          vf[b][n] = *reinterpret_cast<const u32x2*>(vp + 256 * n + 16 * r + 4 * g4);
-        // Zero-fill keys at or past k_len (never-written slots may hold NaN).
-        const int nl = nvalid - 4 * g4;  // valid keys among this lane's four
-        const uint32_t m0 = nl >= 2 ? 0xffffffffu : (nl == 1 ? 0x0000ffffu : 0u);
-        const uint32_t m1 = nl >= 4 ? 0xffffffffu : (nl == 3 ? 0x0000ffffu : 0u);
-#pragma unroll
-        for (int n = 0; n < NBLK; ++n) {
-          vf[b][n].x &= m0;
-          vf[b][n].y &= m1;
-        }
-        if (r >= nvalid) {
-#pragma unroll
-          for (int st = 0; st < NSTEP; ++st) kf[b][st] = u32x4{0u, 0u, 0u, 0u};
-        }
-      } else {
-#pragma unroll
-        for (int st = 0; st < NSTEP; ++st) kf[b][st] = u32x4{0u, 0u, 0u, 0u};
-#pragma unroll
-        for (int n = 0; n < NBLK; ++n) vf[b][n] = u32x2{0u, 0u};
-      }
-    }
-
-    // Scores: lane holds keys kb + 16b + 4*g4 + i (i = 0..3) of its row.
-    float x[2][4];
-#pragma unroll
-    for (int b = 0; b < 2; ++b) {
-      f32x4 sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int st = 0; st < NSTEP; ++st) sc = mfma16x16x32(__builtin_bit_cast(bf16x8, kf[b][st]), qf[st], sc);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 16 * b + 4 * g4 + i;
-        const bool ok = key >= rk_lo && key <= rk_hi;
-        x[b][i] = ok ? sc[i] * a.qk_scale_log2 : -INFINITY;
-      }
-    }
-    float tmax = x[0][0];
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[b][i]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 16));
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32));
-    const bool live = tmax != -INFINITY;  // this row sees at least one key here
-
-    const float m_new = fmaxf(m_run, tmax);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2_hw(m_run - m_new);
-    __bf16 pb[2][4];
-    float rs = 0.f;
-#pragma unroll
-    for (int b = 0; b < 2; ++b)
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = (x[b][i] != -INFINITY) ? exp2_hw(x[b][i] - m_new) : 0.f;
-        pb[b][i] = (__bf16)e;
-        rs += (float)pb[b][i];
-      }
-    rs += __shfl_xor(rs, 16);
-    rs += __shfl_xor(rs, 32);
-    const float l_new = __builtin_fmaf(alpha, l_run, rs);
-
-    const bf16x8 pfrag = {pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
-#pragma unroll
-    for (int n = 0; n < NBLK; ++n) {
-      const u32x4 vv = {vf[0][n].x, vf[0][n].y, vf[1][n].x, vf[1][n].y};
-      const f32x4 cin = acc[n] * alpha;
-      const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag, cin);
-      acc[n] = live ? res : acc[n];
-    }
-    m_run = live ? m_new : m_run;
-    l_run = live ? l_new : l_run;
-  }
-
-  if (rk_lo <= rk_hi) {
-    const int64_t row = (int64_t)(q0 + tq0 + t) * a.num_q_heads + (kvh << a.log2_group) + hh;
-    const int64_t idx = row * a.ns + sigma;
-    if (g4 == 0) a.ws_ml[idx] = make_float2(m_run, l_run);
-    float* ap = a.ws_acc + idx * D;
-#pragma unroll
-    for (int n = 0; n < NBLK; ++n) *reinterpret_cast<f32x4*>(ap + 16 * n + 4 * g4) = acc[n];
+  // Wave index, made visibly wave-uniform so everything derived from the
+  // item index stays in scalar registers (scalar page-table loads).
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  SplitWave<D> w{a};
+  w.lane = lane;
+  w.g4 = lane >> 4;
+  w.total = ldc(a.plan, a.num_seqs);
+  w.stride = gridDim.x * kSplitWaves;
+  w.u = blockIdx.x * kSplitWaves + wave;
+  w.cur = decode_item(a, w.u, w.total);
+  if (!w.cur.valid) return;
+  w.curL = item_lane<D>(a, w.cur, lane);
+  w.nxt = decode_item(a, w.u + w.stride, w.total);
+  w.st.init();
+  w.ct = w.cur.tile_begin;
+  TileData<D> buf0, buf1;
+  load_tile(a, w.cur.kvh, w.cur.k_len, w.ct, w.cur.tile_end, tile_pages(w.cur.pt_row, w.cur.last_entry, w.ct),
+            lane, buf0);
+  while (w.step(buf0, buf1) && w.step(buf1, buf0)) {
   }
 }
 
@@ -296,12 +506,31 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   *reinterpret_cast<u32x2*>(op) = __builtin_bit_cast(u32x2, o);
 }
 
+// Workgroups of the persistent split kernel that the current device keeps
+// resident at once (computed once per device and head size).
+template <int D>
+int resident_split_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<D>, 64 * kSplitWaves, 0) !=
+      hipSuccess)
+    return 0;
+  cached[dev] = max(1, cus * max(per_cu, 1));
+  return cached[dev];
+}
+
 template <int D>
 hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
-  const int tq = kRowsPerBlock >> a.log2_group;
-  const int nblocks = a.num_tokens / tq + a.num_seqs;
-  dim3 grid(nblocks, a.num_kv_heads, (a.ns + kSplitWaves - 1) / kSplitWaves);
-  hipLaunchKernelGGL(attn_split_kernel<D>, grid, dim3(64 * kSplitWaves), 0, stream, a);
+  const int groups = resident_split_groups<D>();
+  if (groups <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_split_kernel<D>, dim3(groups), dim3(64 * kSplitWaves), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -11,7 +11,7 @@ namespace bi {
 constexpr int kRowsPerBlock = 16;
 // Key tile: two pages of 16 tokens, the K extent of one 16x16x32 MFMA.
 constexpr int kKeyTile = 32;
-// Waves per attention workgroup; each wave owns one key split.
+// Waves per attention split workgroup (each wave works through its own items).
 constexpr int kSplitWaves = 4;
 
 struct AttnSplitArgs {
@@ -35,6 +35,7 @@ struct AttnSplitArgs {
   float qk_scale_log2;       // scale * log2(e)
   float2* ws_ml;             // [R][ns]
   float* ws_acc;             // [R][ns][D]
+  int32_t* plan;             // [num_seqs + 1]: first work item of each sequence, total last
 };
 
 struct AttnMergeArgs {

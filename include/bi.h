@@ -144,13 +144,15 @@ bi_status bi_kv_write(const bi_attn_config* cfg,
 /*                                                                           */
 /* Workspace (caller-owned device memory, contents scratch between calls):   */
 /*   NS = ceil(max_seq_len / S); R = num_tokens * H_q                        */
-/*   ml : float2 [R][NS]      (m, l) of each split, m in base-2 units:       */
-/*        m = max_j y_j, l = sum_j 2^(y_j - m), y_j = scale*log2(e)*<q,k_j>  */
-/*   acc: float  [R][NS][D]   sum_j 2^(y_j - m) v_j, starting at the first   */
-/*        256-byte boundary after ml                                         */
+/*   ml  : float2 [R][NS]     (m, l) of each split, m in base-2 units:       */
+/*         m = max_j y_j, l = sum_j 2^(y_j - m), y_j = scale*log2(e)*<q,k_j> */
+/*   acc : float  [R][NS][D]  sum_j 2^(y_j - m) v_j, at the first 256-byte   */
+/*         boundary after ml                                                 */
+/*   plan: int32  [num_seqs+1] first work item of each sequence (the split   */
+/*         phase's own schedule), at the first 256-byte boundary after acc   */
 /* Only the splits that meet [lo, p] of a row are written and read.          */
 /* ------------------------------------------------------------------------ */
-bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_tokens,
+bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                             int32_t max_seq_len, size_t* bytes);
 
 bi_status bi_paged_attention(const bi_attn_config* cfg,
@@ -240,9 +242,9 @@ bi_status bi_splitk_attention_heuristic(const bi_attn_config* cfg, int32_t num_s
                                         int32_t max_seq_len, int32_t num_compute_units,
                                         int32_t waves_per_cu, int32_t* num_splits_out);
 
-bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_tokens,
-                                                   int32_t max_seq_len, int32_t num_splits,
-                                                   size_t* bytes);
+bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_seqs,
+                                                   int32_t num_tokens, int32_t max_seq_len,
+                                                   int32_t num_splits, size_t* bytes);
 
 /* Same kernels as bi_paged_attention, with the split length derived from
  * num_splits and max_seq_len instead of the configuration's fixed size. */

@@ -48,12 +48,13 @@ def test_config_create(geom, status):
 
 def test_workspace_size_matches_documented_layout():
     cfg = bi.AttnConfig(32, 8, 128, split_size=256)
-    T, L = 7, 1000
+    B, T, L = 3, 7, 1000
     ns = -(-L // 256)
     R = T * 32
     ml = R * ns * 8
-    expect = (ml + 255) // 256 * 256 + R * ns * 128 * 4
-    assert bi.bi_paged_attention_workspace_size(cfg, T, L) == expect
+    acc_end = (ml + 255) // 256 * 256 + R * ns * 128 * 4
+    expect = (acc_end + 255) // 256 * 256 + (B + 1) * 4
+    assert bi.bi_paged_attention_workspace_size(cfg, B, T, L) == expect
     assert bi.bi_kv_cache_bytes(cfg, 10) == 10 * 8 * 128 * 16 * 2
 
 

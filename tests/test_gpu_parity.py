@@ -137,7 +137,7 @@ def test_split_phase_partials_parity():
     qsl_h = np.array([0, 3, 23])
     qsl = torch.tensor(qsl_h, dtype=torch.int32, device=DEV)
     q = torch.cat([reqs[0].q[97:100], reqs[1].q[50:70]]).to(DEV)
-    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, 23, 100))
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, 2, 23, 100))
     bi.bi_paged_attention_split(cfg, q, kv.k, kv.v, pt, sl, qsl, 100, ws)
     ns = 4
     ml, acc = bi.workspace_views(cfg, ws, 23, ns)
@@ -162,7 +162,7 @@ def test_merge_phase_parity_on_synthetic_partials():
     m = (torch.rand((T * H, ns), generator=rng) * 20 - 10).double()
     l = (torch.rand((T * H, ns), generator=rng) * 30 + 1).double()
     a = torch.randn((T * H, ns, D), generator=rng).double() * l[:, :, None]
-    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, T, L))
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, 1, T, L))
     ml, acc = bi.workspace_views(cfg, ws, T, ns)
     ml[:, :, 0] = m.float().to(DEV)
     ml[:, :, 1] = l.float().to(DEV)
