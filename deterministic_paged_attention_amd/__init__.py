@@ -153,7 +153,7 @@ class AttnConfig:
 
     def __del__(self):
         h = getattr(self, "handle", None)
-        if h is not None and h.value:
+        if h is not None and h.value and lib is not None:  # lib may be gone at interpreter exit
             lib.bi_attn_config_destroy(h)
             self.handle = None
 
@@ -161,7 +161,7 @@ class AttnConfig:
         return (num_pages, self.num_kv_heads, self.head_dim // 8, self.page_size, 8)
 
     def v_cache_shape(self, num_pages) -> Tuple[int, ...]:
-        return (num_pages, self.num_kv_heads, self.head_dim, self.page_size)
+        return (num_pages, self.num_kv_heads, self.head_dim // 32, 16, self.page_size, 2)
 
 
 def bi_attn_config_create(num_q_heads, num_kv_heads, head_dim, page_size=16, split_size=256, window=0, scale=0.0):

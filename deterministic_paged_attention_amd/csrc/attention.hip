@@ -29,8 +29,8 @@
 // of v_mfma_f32_16x16x32_bf16 (S^T = K Q^T), the score fragments that come out
 // are exactly the B operand of the PV product (O^T = V^T P^T), and the V
 // fragments are read straight into its A operand.  The cache layouts
-// (K [page][h][D/8][16][8], V [page][h][D][16]) make every one of these reads
-// a fully used contiguous run of 512 B or 1 KiB per wave instruction.
+// (K [page][h][D/8][16][8], V [page][h][D/32][16][16][2]) make every one of
+// these reads a fully used contiguous KiB per wave instruction.
 
 #include "bi_internal.h"
 
@@ -109,7 +109,7 @@ struct SplitState {
 template <int D>
 struct TileData {
   u32x4 kf[2][D / 32];   // K rows: A operand of S^T = K Q^T
-  u32x2 vf[2][D / 16];   // V^T fragments: A operand of O^T = V^T P^T
+  u32x4 vf[2][D / 32];   // V^T fragments of two head-dim blocks, interleaved (see load_tile)
   u32x2 vmask[2];        // per page: keeps the bits of this lane's keys below k_len
 };
 
@@ -151,6 +151,7 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
   constexpr int NSTEP = D / 32;
   constexpr int NBLK = D / 16;
   constexpr int PAGE_BYTES = D * 16 * 2;
+  (void)NSTEP;
   const int r = lane & 15, g4 = lane >> 4;
   const int64_t head_elems = (int64_t)D * 16;
   const bool live_tile = tile < tile_end;
@@ -172,9 +173,13 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 #pragma unroll
     for (int st = 0; st < NSTEP; ++st)
       t.kf[b][st] = __builtin_amdgcn_raw_buffer_load_b128(kr, (64 * st + lane) * 16, 0, kStreamLoad);
+    // V page layout [D/32][16][16][2]: head-dim d = 32*np + 16*e + r, token o at
+    // ((np*16 + r)*16 + o)*2 + e.  One 16-byte load gives this lane tokens
+    // 4*g4 .. 4*g4+3 of rows d = 32*np + r (e = 0) and 32*np + 16 + r (e = 1);
+    // per np the 64 lanes read one contiguous KiB.
 #pragma unroll
-    for (int n = 0; n < NBLK; ++n)
-      t.vf[b][n] = __builtin_amdgcn_raw_buffer_load_b64(vr, (256 * n + 16 * r + 4 * g4) * 2, 0, kStreamLoad);
+    for (int np = 0; np < NBLK / 2; ++np)
+      t.vf[b][np] = __builtin_amdgcn_raw_buffer_load_b128(vr, ((np * 16 + r) * 16 + 4 * g4) * 4, 0, kStreamLoad);
   }
 }
 
@@ -226,8 +231,14 @@ __device__ __forceinline__ void compute_tile(SplitState<D>& st, const TileData<D
   const bf16x8 pfrag = {pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
 #pragma unroll
   for (int n = 0; n < NBLK; ++n) {
-    const u32x4 vv = {t.vf[0][n].x & t.vmask[0].x, t.vf[0][n].y & t.vmask[0].y, t.vf[1][n].x & t.vmask[1].x,
-                      t.vf[1][n].y & t.vmask[1].y};
+    // De-interleave head-dim block n (e = n & 1) from the loaded pairs:
+    // dword j of vf holds token j of rows e = 0 (low half) and e = 1 (high half).
+    const uint32_t sel = (n & 1) ? 0x07060302u : 0x05040100u;
+    const u32x4 w0 = t.vf[0][n >> 1], w1 = t.vf[1][n >> 1];
+    const u32x4 vv = {__builtin_amdgcn_perm(w0.y, w0.x, sel) & t.vmask[0].x,
+                      __builtin_amdgcn_perm(w0.w, w0.z, sel) & t.vmask[0].y,
+                      __builtin_amdgcn_perm(w1.y, w1.x, sel) & t.vmask[1].x,
+                      __builtin_amdgcn_perm(w1.w, w1.z, sel) & t.vmask[1].y};
     const f32x4 cin = st.acc[n] * alpha;
     const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag, cin);
     st.acc[n] = live ? res : st.acc[n];
@@ -384,10 +395,16 @@ __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item
   const int hh = r & ((1 << a.log2_group) - 1);
   const int64_t row = (int64_t)(it.q0 + it.tq0 + t) * a.num_q_heads + (it.kvh << a.log2_group) + hh;
   const int64_t idx = row * a.ns + it.sigma;
-  if (g4 == 0) a.ws_ml[idx] = make_float2(st.m, st.l);
+  // Partials are written once and read once by the merge: non-temporal
+  // stores keep them from competing with the K/V stream for L2.
+  if (g4 == 0) {
+    float* mlp = reinterpret_cast<float*>(a.ws_ml + idx);
+    __builtin_nontemporal_store(st.m, mlp);
+    __builtin_nontemporal_store(st.l, mlp + 1);
+  }
   float* ap = a.ws_acc + idx * D;
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n) *reinterpret_cast<f32x4*>(ap + 16 * n + 4 * g4) = st.acc[n];
+  for (int n = 0; n < D / 16; ++n) __builtin_nontemporal_store(st.acc[n], reinterpret_cast<f32x4*>(ap + 16 * n + 4 * g4));
 }
 
 // ---------------------------------------------------------------------------
@@ -488,10 +505,14 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   }
   const float2* ml = a.ws_ml + row * a.ns;
   float mstar = -INFINITY;
+#pragma unroll 8
   for (int sg = sig_lo; sg <= sig_hi; ++sg) mstar = fmaxf(mstar, ml[sg].x);
   float L = 0.f;
   f32x4 N = {0.f, 0.f, 0.f, 0.f};
   const float* ap = a.ws_acc + row * a.ns * D + 4 * dq;
+  // Unrolled so the loads of several splits are in flight together; the
+  // accumulation itself stays in increasing split order.
+#pragma unroll 8
   for (int sg = sig_lo; sg <= sig_hi; ++sg) {
     const float2 v = ml[sg];
     const float w = exp2_hw(v.x - mstar);

@@ -47,7 +47,8 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_t
 
 // One thread per (token, KV head, 8-element head-dim chunk c).
 // K cache [page][h][D/8][16][8]: the chunk is one 16-byte store.
-// V cache [page][h][D][16]:      eight 2-byte stores, one per head-dim row.
+// V cache [page][h][D/32][16][16][2] (head-dim d = 32*np + 16*e + r, token o at
+// ((np*16 + r)*16 + o)*2 + e): eight 2-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
                                                        const uint16_t* v_new, int64_t v_stride,
@@ -69,11 +70,13 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const u
   const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + (int64_t)t * k_stride + h * D + 8 * c);
   *reinterpret_cast<u32x4*>(k_cache + head_base + (c * 16 + o) * 8) = kv;
   const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + (int64_t)t * v_stride + h * D + 8 * c);
-  uint16_t* vd = v_cache + head_base + (int64_t)(8 * c) * 16 + o;
+  // d = 8c + i: np = c / 4, e = (c / 2) & 1, r = 8 * (c & 1) + i.
+  const int np = c >> 2, ev = (c >> 1) & 1, r0 = 8 * (c & 1);
+  uint16_t* vd = v_cache + head_base + ((int64_t)(np * 16 + r0) * 16 + o) * 2 + ev;
 #pragma unroll
-  for (int e = 0; e < 4; ++e) {
-    vd[(2 * e) * 16] = (uint16_t)(vv[e] & 0xffffu);
-    vd[(2 * e + 1) * 16] = (uint16_t)(vv[e] >> 16);
+  for (int i = 0; i < 4; ++i) {
+    vd[(2 * i) * 32] = (uint16_t)(vv[i] & 0xffffu);
+    vd[(2 * i + 1) * 32] = (uint16_t)(vv[i] >> 16);
   }
 }
 

@@ -87,8 +87,9 @@ bi_status bi_attn_config_query(const bi_attn_config* cfg, bi_attn_desc* desc_out
 /* Paged KV cache layout (one layer), bf16, owned by the caller:             */
 /*   K: [num_pages][H_kv][D/8][P][8]   (8 head-dim elements of one token are */
 /*       contiguous; the 16 tokens of a page follow each other per 8-chunk)  */
-/*   V: [num_pages][H_kv][D][P]        (the P tokens of one head-dim index   */
-/*       are contiguous)                                                     */
+/*   V: [num_pages][H_kv][D/32][16][P][2]  element (np, r, o, e) holds token */
+/*       o at head-dim d = 32*np + 16*e + r (two head-dim rows 16 apart are  */
+/*       interleaved token by token)                                         */
 /* Page table: int32 [num_seqs][page_table_stride]; entry i of sequence s is */
 /* the physical page holding logical positions [i*P, (i+1)*P).  Entries past */
 /* ceil(k_len/P) are never read.                                             */

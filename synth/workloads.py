@@ -31,7 +31,7 @@ class DecodeWorkload:
     k_new: torch.Tensor       # [B, H_kv, D] bf16 (this step's token)
     v_new: torch.Tensor
     k_cache: torch.Tensor     # [pages, H_kv, D/8, 16, 8] bf16
-    v_cache: torch.Tensor     # [pages, H_kv, D, 16] bf16
+    v_cache: torch.Tensor     # [pages, H_kv, D/32, 16, 16, 2] bf16
     page_table: torch.Tensor  # [B, stride] int32
     seq_lens: torch.Tensor    # [B] int32
     qsl: torch.Tensor         # [B+1] int32
@@ -50,7 +50,7 @@ class DecodeWorkload:
         vp = self.v_cache.index_select(0, idx).cpu()
         npg = len(self.pages[s])
         k = kp.permute(0, 3, 1, 2, 4).reshape(npg, self.page_size, self.num_kv_heads, self.head_dim)
-        v = vp.permute(0, 3, 1, 2)
+        v = vp.permute(0, 4, 1, 2, 5, 3).reshape(npg, self.page_size, self.num_kv_heads, self.head_dim)
         return to_f64(k), to_f64(v), np.arange(npg)[None, :], self.lengths[s]
 
     def kv_bytes(self) -> int:
@@ -75,7 +75,7 @@ def build_decode_workload(num_q_heads: int, num_kv_heads: int, head_dim: int, ba
         pt[s, :len(row)] = torch.tensor(row, dtype=torch.int32)
     H, D = num_kv_heads, head_dim
     k_cache = normal_bf16_device((num_pages, H, D // 8, page_size, 8), seed + 2, device)
-    v_cache = normal_bf16_device((num_pages, H, D, page_size), seed + 3, device)
+    v_cache = normal_bf16_device((num_pages, H, D // 32, 16, page_size, 2), seed + 3, device)
     q = normal_bf16_device((batch, num_q_heads, D), seed + 4, device)
     k_new = normal_bf16_device((batch, H, D), seed + 5, device)
     v_new = normal_bf16_device((batch, H, D), seed + 6, device)

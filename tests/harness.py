@@ -34,8 +34,10 @@ def logical_k(k_cache: torch.Tensor) -> np.ndarray:
 
 
 def logical_v(v_cache: torch.Tensor) -> np.ndarray:
-    """[pages][H][D][16] -> [pages][16][H][D] float64 (documented V layout)."""
-    return synth.to_f64(v_cache.cpu().permute(0, 3, 1, 2))
+    """[pages][H][D/32][16 r][16 tok][2 e] -> [pages][16][H][D] float64, d = 32*np + 16*e + r
+    (documented V layout)."""
+    pg, H, nq, R, P, E = v_cache.shape
+    return synth.to_f64(v_cache.cpu().permute(0, 4, 1, 2, 5, 3).reshape(pg, P, H, nq * E * R))
 
 
 @dataclasses.dataclass
