@@ -21,7 +21,7 @@ HEADER_PATH = os.path.join(os.path.dirname(_PKG), "include", "bi.h")
 
 if not os.path.exists(LIB_PATH):
     raise ImportError(f"{LIB_PATH} is missing: build it first with "
-                      "`python -m deterministic_paged_attention_amd.build` (or __graft_entry__.build())")
+                      "`python deterministic_paged_attention_amd/build.py` (or __graft_entry__.build())")
 
 # torch is imported first so that its HIP runtime is the one loaded into the
 # process: libbi.so then binds to that same libamdhip64 (same soname) instead of
@@ -81,6 +81,11 @@ _sig("bi_gemm_splitk_heuristic", c_i32, c_i64)
 _sig("bi_gemm_splitk_workspace_size", c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_gemm_splitk", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_i32, c_vp, c_sz,
      c_vp)
+_sig("bi_embedding", c_i32, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_i64, c_vp)
+_sig("bi_qk_norm_rope", c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
+     ctypes.c_double, c_vp)
+_sig("bi_add", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
+_sig("bi_gated_gelu", c_i32, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_status_string", ctypes.c_char_p, c_i32)
 _sig("bi_last_error_message", ctypes.c_char_p)
 _sig("bi_version", c_i32)
@@ -354,6 +359,56 @@ def bi_gemm_splitk(a, w, k_splits, out_dtype=None, out=None, workspace=None, str
         workspace = alloc_workspace(need.value, a.device)
     _check(lib.bi_gemm_splitk(*args, k_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
+    return out
+
+
+def bi_embedding(table, ids, out=None, stream=None):
+    torch = _torch()
+    _need(table, torch.bfloat16, "table")
+    _need(ids, torch.int32, "ids")
+    V, H = table.shape
+    T = ids.shape[0]
+    if out is None:
+        out = torch.empty((T, H), dtype=torch.bfloat16, device=table.device)
+    ld = out.stride(0) if T > 1 else H
+    _check(lib.bi_embedding(_ptr(table), V, H, _ptr(ids), T, _ptr(out), ld, _stream(stream)))
+    return out
+
+
+def bi_qk_norm_rope(qkv, seq_lens, query_start_loc, num_q_heads, num_kv_heads, head_dim, gamma_q, gamma_k, eps,
+                    rope_theta, stream=None):
+    """In place on the q and k parts of qkv [T, row] (bf16)."""
+    torch = _torch()
+    _need(qkv, torch.bfloat16, "qkv")
+    T = qkv.shape[0]
+    rs = qkv.stride(0) if T > 1 else qkv.shape[1]
+    _check(lib.bi_qk_norm_rope(_ptr(qkv), rs, T, _ptr(seq_lens), _ptr(query_start_loc), seq_lens.shape[0],
+                               num_q_heads, num_kv_heads, head_dim, _ptr(gamma_q), _ptr(gamma_k), float(eps),
+                               float(rope_theta), _stream(stream)))
+    return qkv
+
+
+def bi_add(a, b, out=None, stream=None):
+    torch = _torch()
+    _need(a, torch.bfloat16, "a")
+    _need(b, torch.bfloat16, "b")
+    R, N = a.shape
+    if out is None:
+        out = torch.empty((R, N), dtype=torch.bfloat16, device=a.device)
+    ld = lambda t: t.stride(0) if R > 1 else N  # noqa: E731
+    _check(lib.bi_add(_ptr(a), ld(a), _ptr(b), ld(b), _ptr(out), ld(out), R, N, _stream(stream)))
+    return out
+
+
+def bi_gated_gelu(x, out=None, stream=None):
+    torch = _torch()
+    _need(x, torch.bfloat16, "x")
+    R, F2 = x.shape
+    F = F2 // 2
+    if out is None:
+        out = torch.empty((R, F), dtype=torch.bfloat16, device=x.device)
+    _check(lib.bi_gated_gelu(_ptr(x), x.stride(0) if R > 1 else F2, _ptr(out), out.stride(0) if R > 1 else F, R, F,
+                             _stream(stream)))
     return out
 
 

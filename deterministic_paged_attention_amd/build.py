@@ -1,6 +1,6 @@
 """Build libbi.so in-tree with hipcc for gfx950.
 
-    python -m deterministic_paged_attention_amd.build
+    python deterministic_paged_attention_amd/build.py
 
 Each .hip source is compiled to an object (in parallel), then linked into
 ``deterministic_paged_attention_amd/libbi.so``.  Floating-point policy: no
@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip"]
+SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip", "glue.hip"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"

@@ -446,6 +446,60 @@ bi_status bi_gemm(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw
                     "gemm launch");
 }
 
+bi_status bi_embedding(const void* table_dev, int64_t vocab, int64_t hidden, const int32_t* ids_dev,
+                       int32_t num_tokens, void* out_dev, int64_t ld_out, void* stream) {
+  if (vocab < 1 || hidden < 8 || hidden % 8 || num_tokens < 0 || ld_out < hidden || ld_out % 8)
+    return fail(BI_ERR_INVALID_ARG, "vocab >= 1, hidden a positive multiple of 8, ld_out >= hidden (multiple of 8)");
+  if (num_tokens == 0) return ok();
+  if (!table_dev || !ids_dev || !out_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(table_dev, 16) || !aligned(out_dev, 16)) return fail(BI_ERR_INVALID_ARG, "table and out must be 16-byte aligned");
+  return hip_status(bi::launch_embedding((const uint16_t*)table_dev, vocab, hidden, ids_dev, num_tokens,
+                                         (uint16_t*)out_dev, ld_out, (hipStream_t)stream),
+                    "embedding launch");
+}
+
+bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens, const int32_t* seq_lens_dev,
+                          const int32_t* query_start_loc_dev, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, const void* gamma_q_dev, const void* gamma_k_dev,
+                          float eps, double rope_theta, void* stream) {
+  if (num_seqs < 1 || num_tokens < 0 || num_q_heads < 1 || num_kv_heads < 1)
+    return fail(BI_ERR_INVALID_ARG, "num_seqs, num_q_heads, num_kv_heads >= 1 and num_tokens >= 0 required");
+  if (head_dim != 64 && head_dim != 128 && head_dim != 256)
+    return fail(BI_ERR_UNSUPPORTED_CONFIG, "head_dim %d: this build supports 64, 128, 256", head_dim);
+  if (row_stride < (int64_t)(num_q_heads + num_kv_heads) * head_dim)
+    return fail(BI_ERR_INVALID_ARG, "row_stride smaller than the q and k parts of a row");
+  if (!(eps >= 0.f) || std::isinf(eps) || !(rope_theta > 1.0) || std::isinf(rope_theta))
+    return fail(BI_ERR_INVALID_ARG, "eps must be finite and >= 0, rope_theta finite and > 1");
+  if (num_tokens == 0) return ok();
+  if (!qkv_dev || !seq_lens_dev || !query_start_loc_dev || !gamma_q_dev || !gamma_k_dev)
+    return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  return hip_status(bi::launch_qk_norm_rope((uint16_t*)qkv_dev, row_stride, num_tokens, seq_lens_dev,
+                                            query_start_loc_dev, num_seqs, num_q_heads, num_kv_heads, head_dim,
+                                            (const uint16_t*)gamma_q_dev, (const uint16_t*)gamma_k_dev, eps,
+                                            rope_theta, (hipStream_t)stream),
+                    "qk_norm_rope launch");
+}
+
+bi_status bi_add(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* c_dev, int64_t ldc,
+                 int64_t rows, int64_t n, void* stream) {
+  if (rows < 0 || n < 0 || lda < n || ldb < n || ldc < n) return fail(BI_ERR_INVALID_ARG, "bad add shape");
+  if (rows * n == 0) return ok();
+  if (!a_dev || !b_dev || !c_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  return hip_status(bi::launch_add((const uint16_t*)a_dev, lda, (const uint16_t*)b_dev, ldb, (uint16_t*)c_dev, ldc,
+                                   rows, n, (hipStream_t)stream),
+                    "add launch");
+}
+
+bi_status bi_gated_gelu(const void* in_dev, int64_t ld_in, void* out_dev, int64_t ld_out, int64_t rows, int64_t ffn,
+                        void* stream) {
+  if (rows < 0 || ffn < 1 || ld_in < 2 * ffn || ld_out < ffn) return fail(BI_ERR_INVALID_ARG, "bad gated_gelu shape");
+  if (rows == 0) return ok();
+  if (!in_dev || !out_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  return hip_status(bi::launch_gated_gelu((const uint16_t*)in_dev, ld_in, (uint16_t*)out_dev, ld_out, rows, ffn,
+                                          (hipStream_t)stream),
+                    "gated_gelu launch");
+}
+
 int32_t bi_gemm_splitk_heuristic(int64_t M) { return M <= 16 ? 8 : (M <= 128 ? 4 : 1); }
 
 bi_status bi_gemm_splitk_workspace_size(int64_t M, int64_t N, int32_t k_splits, size_t* bytes) {

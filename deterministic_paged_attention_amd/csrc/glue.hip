@@ -1,0 +1,163 @@
+// Per-row and elementwise glue of a decoder step: embedding gather, per-head
+// q/k RMSNorm fused with rotary position embedding, residual add, gated GELU.
+//
+// The pages define the step only as the cold causal forward Forward(W, h)
+// (Vosti deep-dive blog (深入解析 Vosti), §2, Theorem 4.1); the layer details
+// here are the plainest Gemma-3-style choices (pre-norm blocks, q/k norm,
+// half-rotation RoPE, tanh-approximated gated GELU).  Every output element
+// depends only on its own row (token) and, for RoPE, its logical position —
+// never on the batch — and every reduction has a tree fixed by the row size.
+
+#include "bi_internal.h"
+
+#include <math.h>
+
+namespace bi {
+namespace {
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
+
+__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int t) {
+  int lo = 0, hi = num_seqs - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// out[t, :] = table[ids[t], :]; rows with an id outside [0, vocab) are zero.
+__global__ __launch_bounds__(256) void embedding_kernel(const uint16_t* table, int64_t vocab, int64_t hidden,
+                                                        const int32_t* ids, int32_t num_tokens, uint16_t* out,
+                                                        int64_t ld_out) {
+  const int64_t nch = hidden / 8;
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= (int64_t)num_tokens * nch) return;
+  const int64_t t = gid / nch, c = gid % nch;
+  const int32_t id = ids[t];
+  u32x4 v = {0u, 0u, 0u, 0u};
+  if (id >= 0 && id < vocab) v = *reinterpret_cast<const u32x4*>(table + (int64_t)id * hidden + 8 * c);
+  *reinterpret_cast<u32x4*>(out + t * ld_out + 8 * c) = v;
+}
+
+// One wave per (token, head) row of the q and k parts of a fused QKV row.
+//   y = x / sqrt(sum x^2 / D + eps) * gamma         (fp32; fixed tree over D)
+//   z_i       = y_i cos(a_i) - y_{i+D/2} sin(a_i)
+//   z_{i+D/2} = y_i sin(a_i) + y_{i+D/2} cos(a_i),  a_i = p * theta^(-2i/D),  i < D/2
+// with p = k_len - q_len + j the row's logical position.  The angle and its
+// sine and cosine are evaluated in fp64 and rounded once to fp32; the result
+// is rounded once to bf16 and written in place.
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_t row_stride, int32_t num_tokens,
+                                                           const int32_t* seq_lens, const int32_t* qsl,
+                                                           int32_t num_seqs, int32_t num_q_heads,
+                                                           int32_t num_kv_heads, int32_t head_dim,
+                                                           const uint16_t* gamma_q, const uint16_t* gamma_k,
+                                                           float eps, double log2_theta) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = num_q_heads + num_kv_heads;
+  if (row >= (int64_t)num_tokens * heads) return;
+  const int t = (int)(row / heads);
+  const int h = (int)(row % heads);
+  const int s = find_token_seq(qsl, num_seqs, t);
+  const int p = seq_lens[s] - (qsl[s + 1] - qsl[s]) + (t - qsl[s]);
+  uint16_t* x = qkv + (int64_t)t * row_stride + (int64_t)h * head_dim;
+  const uint16_t* g = h < num_q_heads ? gamma_q : gamma_k;
+  const int half = head_dim / 2;
+  // This lane owns the pairs (i, i + D/2) for i = lane, lane + 64, ...  (at most 2 for D <= 256).
+  float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
+  float ss = 0.f;
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    if (i < half) {
+      a[j] = bf16_to_f32(x[i]);
+      b[j] = bf16_to_f32(x[i + half]);
+      ss = __builtin_fmaf(a[j], a[j], ss);
+      ss = __builtin_fmaf(b[j], b[j], ss);
+    }
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) ss += __shfl_xor(ss, off);
+  const float inv = 1.0f / __builtin_sqrtf(ss / (float)head_dim + eps);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int i = lane + 64 * j;
+    if (i < half) {
+      const float ya = (a[j] * inv) * bf16_to_f32(g[i]);
+      const float yb = (b[j] * inv) * bf16_to_f32(g[i + half]);
+      const double ang = (double)p * exp2(-(double)(2 * i) / (double)head_dim * log2_theta);
+      const float c = (float)cos(ang), sn = (float)sin(ang);
+      x[i] = f32_to_bf16(ya * c - yb * sn);
+      x[i + half] = f32_to_bf16(ya * sn + yb * c);
+    }
+  }
+}
+
+// c = a + b elementwise in fp32, one bf16 rounding; rows of length n with strides.
+__global__ __launch_bounds__(256) void add_kernel(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb,
+                                                  uint16_t* c, int64_t ldc, int64_t rows, int64_t n) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= rows * n) return;
+  const int64_t r = gid / n, i = gid % n;
+  c[r * ldc + i] = f32_to_bf16(bf16_to_f32(a[r * lda + i]) + bf16_to_f32(b[r * ldb + i]));
+}
+
+// out[t, i] = gelu(gate[t, i]) * up[t, i], gate = in[t, 0:F], up = in[t, F:2F];
+// gelu(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), fp32, one bf16 rounding.
+__global__ __launch_bounds__(256) void gated_gelu_kernel(const uint16_t* in, int64_t ld_in, uint16_t* out,
+                                                         int64_t ld_out, int64_t rows, int64_t F) {
+  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (gid >= rows * F) return;
+  const int64_t r = gid / F, i = gid % F;
+  const float x = bf16_to_f32(in[r * ld_in + i]);
+  const float u = bf16_to_f32(in[r * ld_in + F + i]);
+  const float inner = 0.7978845608028654f * (x + 0.044715f * x * x * x);
+  const float gl = 0.5f * x * (1.0f + tanhf(inner));
+  out[r * ld_out + i] = f32_to_bf16(gl * u);
+}
+
+unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
+
+}  // namespace
+
+hipError_t launch_embedding(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* ids,
+                            int32_t num_tokens, uint16_t* out, int64_t ld_out, hipStream_t stream) {
+  const int64_t n = (int64_t)num_tokens * (hidden / 8);
+  if (n == 0) return hipSuccess;
+  hipLaunchKernelGGL(embedding_kernel, dim3(blocks_for(n)), dim3(256), 0, stream, table, vocab, hidden, ids,
+                     num_tokens, out, ld_out);
+  return hipGetLastError();
+}
+
+hipError_t launch_qk_norm_rope(uint16_t* qkv, int64_t row_stride, int32_t num_tokens, const int32_t* seq_lens,
+                               const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
+                               int32_t head_dim, const uint16_t* gamma_q, const uint16_t* gamma_k, float eps,
+                               double theta, hipStream_t stream) {
+  const int64_t rows = (int64_t)num_tokens * (num_q_heads + num_kv_heads);
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, qkv, row_stride,
+                     num_tokens, seq_lens, qsl, num_seqs, num_q_heads, num_kv_heads, head_dim, gamma_q, gamma_k,
+                     eps, log2(theta));
+  return hipGetLastError();
+}
+
+hipError_t launch_add(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, uint16_t* c, int64_t ldc,
+                      int64_t rows, int64_t n, hipStream_t stream) {
+  if (rows * n == 0) return hipSuccess;
+  hipLaunchKernelGGL(add_kernel, dim3(blocks_for(rows * n)), dim3(256), 0, stream, a, lda, b, ldb, c, ldc, rows, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_gated_gelu(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int64_t rows,
+                             int64_t F, hipStream_t stream) {
+  if (rows * F == 0) return hipSuccess;
+  hipLaunchKernelGGL(gated_gelu_kernel, dim3(blocks_for(rows * F)), dim3(256), 0, stream, in, ld_in, out, ld_out,
+                     rows, F);
+  return hipGetLastError();
+}
+
+}  // namespace bi

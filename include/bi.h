@@ -209,6 +209,44 @@ bi_status bi_gemm(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw
                   int64_t M, int64_t N, int64_t K, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Decoder-step glue.  The pages define the step only as the cold causal     */
+/* forward Forward(W, h) (Vosti deep-dive blog, §2, Theorem 4.1); the layer  */
+/* details are the plainest Gemma-3-style choices.  Each output element      */
+/* depends on its own row (token) only, and on the row's logical position    */
+/* for RoPE, so all of these are batch-invariant by construction.            */
+/* ------------------------------------------------------------------------ */
+
+/* out[t, :] = table[ids[t], :] (bf16 copy; rows with an id outside
+ * [0, vocab) are zero).  table [vocab][hidden], hidden a multiple of 8;
+ * out rows ld_out elements apart. */
+bi_status bi_embedding(const void* table_dev, int64_t vocab, int64_t hidden, const int32_t* ids_dev,
+                       int32_t num_tokens, void* out_dev, int64_t ld_out, void* stream);
+
+/* In place on the q and k parts of fused QKV rows (token t's row starts at
+ * qkv + t*row_stride: H_q heads of q, then H_kv heads of k, each head_dim
+ * long).  Each head row x is normalised, y = x / sqrt(mean(x^2) + eps) *
+ * gamma (gamma_q for q heads, gamma_k for k heads, bf16 [head_dim]), then
+ * rotated in half-split pairs (i, i + D/2) by the angle p * theta^(-2i/D),
+ * p = seq_lens[s] - q_len_s + j the row's logical position.  fp32
+ * arithmetic, angle and sin/cos in fp64, one bf16 rounding.
+ * head_dim in {64, 128, 256}. */
+bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens, const int32_t* seq_lens_dev,
+                          const int32_t* query_start_loc_dev, int32_t num_seqs, int32_t num_q_heads,
+                          int32_t num_kv_heads, int32_t head_dim, const void* gamma_q_dev,
+                          const void* gamma_k_dev, float eps, double rope_theta, void* stream);
+
+/* c = a + b elementwise (fp32 add, one bf16 rounding); rows x n with row
+ * strides lda, ldb, ldc.  c may alias a or b. */
+bi_status bi_add(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* c_dev, int64_t ldc,
+                 int64_t rows, int64_t n, void* stream);
+
+/* out[r, i] = gelu(in[r, i]) * in[r, ffn + i] for i < ffn, with the tanh
+ * form gelu(x) = 0.5 x (1 + tanh(sqrt(2/pi) (x + 0.044715 x^3))), fp32, one
+ * bf16 rounding. */
+bi_status bi_gated_gelu(const void* in_dev, int64_t ld_in, void* out_dev, int64_t ld_out, int64_t rows,
+                        int64_t ffn, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Host-side plan checks (host arrays; nothing is launched).                 */
 /* ------------------------------------------------------------------------ */
 
