@@ -86,3 +86,25 @@ def build_decode_workload(num_q_heads: int, num_kv_heads: int, head_dim: int, ba
         seq_lens=torch.tensor(lengths, dtype=torch.int32, device=device),
         qsl=torch.arange(batch + 1, dtype=torch.int32, device=device),
         max_seq_len=max(lengths))
+
+
+def decoder_weights(layers: int, hidden: int, q_heads: int, kv_heads: int, head_dim: int, ffn: int, vocab: int,
+                    seed: int, device: str = "cuda") -> dict:
+    """Random-init weights of a pre-norm decoder stack: matrices ~ N(0, 0.02) stored
+    [out, in], norm gains ~ N(1, 0.1), tied embedding [vocab, hidden] ~ N(0, 0.02)."""
+    qkv = (q_heads + 2 * kv_heads) * head_dim
+    out = {"embed": normal_bf16_device((vocab, hidden), seed, device, std=0.02),
+           "g_final": normal_bf16_device((hidden,), seed + 1, device, std=0.1, mean=1.0), "layers": []}
+    for l in range(layers):
+        b = seed + 100 * (l + 1)
+        out["layers"].append({
+            "w_qkv": normal_bf16_device((qkv, hidden), b + 1, device, std=0.02),
+            "w_o": normal_bf16_device((hidden, q_heads * head_dim), b + 2, device, std=0.02),
+            "w_gu": normal_bf16_device((2 * ffn, hidden), b + 3, device, std=0.02),
+            "w_down": normal_bf16_device((hidden, ffn), b + 4, device, std=0.02),
+            "g_attn": normal_bf16_device((hidden,), b + 5, device, std=0.1, mean=1.0),
+            "g_mlp": normal_bf16_device((hidden,), b + 6, device, std=0.1, mean=1.0),
+            "g_q": normal_bf16_device((head_dim,), b + 7, device, std=0.1, mean=1.0),
+            "g_k": normal_bf16_device((head_dim,), b + 8, device, std=0.1, mean=1.0),
+        })
+    return out
