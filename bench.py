@@ -12,6 +12,16 @@ Prints ONE JSON line.  `value` = algorithmic HBM bytes of the whole step / step
 time (GB/s).  `roofline` is for the dominant kernel (attention split phase),
 timed with HIP events recorded on the stream it is launched on.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
+
+Other workloads (one JSON line each, same keys; not the headline):
+  --workload decode-sweep   the same attention layer at batch 1, 8, 64 and 256 (MALL
+                            flushed before every timed repetition), vs split-K
+  --workload gemm           RMSNorm + GEMM, hidden 4096, M in {1, 7, 64, 256, 1024},
+                            N in {14336 (bf16 out), 128256 (fp32 logits)}, vs split-K
+  --workload prefill        chunked prefill with a shared 1024-token prefix (8
+                            requests), chunk budgets {16, 128, 512} and token by token
+  --workload gemma          one decode step of a 34-layer Gemma-3-4B-shaped decoder
+                            (replayed as one HIP graph)
 """
 from __future__ import annotations
 
@@ -101,26 +111,7 @@ def cpu_baseline(wl, sample_seqs: int):
                       f"same workload (same bytes-per-sequence accounting as the GPU), {dt:.1f} s of oracle time"}
 
 
-def main():
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--batch", type=int, default=256)
-    ap.add_argument("--seed", type=int, default=2000)
-    ap.add_argument("--cpu-sample", type=int, default=256)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--no-splitk", action="store_true")
-    ap.add_argument("--copy-calibration-mib", type=int, default=0,
-                    help="also run one plain device copy of this size (for HBM counter calibration)")
-    args = ap.parse_args()
-
-    world = int(os.environ.get("WORLD_SIZE", "1"))
-    if args.gpus != 1 or world != 1:
-        print(f"bench.py measures one GPU only: the method is single-GPU and this build has no multi-GPU path "
-              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
-        sys.exit(2)
-
+def bench_decode(args):
     import torch
     import deterministic_paged_attention_amd as bi
     import synth
@@ -277,6 +268,439 @@ def main():
         "kernel_sha": kernel_source_hash(),
     }
     print(json.dumps(line), flush=True)
+
+
+# ---------------------------------------------------------------------------
+# Secondary workloads (not the headline line).
+# ---------------------------------------------------------------------------
+PEAK_BF16_TFLOPS = 2500.0
+FLUSH_BYTES = 1 << 30   # > the 256 MB MALL
+
+
+def _torch_env():
+    import torch
+    import deterministic_paged_attention_amd as bi
+    import synth
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    return torch, bi, synth
+
+
+def rep_times_ms(fn, reps, flush=None):
+    """Duration (ms) of each of `reps` calls of fn, from HIP events recorded on the
+    current stream around each call; `flush()` runs before each call, untimed."""
+    import torch
+    stream = torch.cuda.current_stream()
+    pairs = []
+    for _ in range(reps):
+        if flush is not None:
+            flush()
+        a = torch.cuda.Event(enable_timing=True)
+        b = torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        pairs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) for a, b in pairs]
+
+
+def pct(ts):
+    import numpy as np
+    return {"median": float(np.median(ts)), "p10": float(np.percentile(ts, 10)), "p90": float(np.percentile(ts, 90))}
+
+
+def mall_flusher():
+    """Evicts the MALL and L2 by reading 1 GiB.  A read, not a write: a write
+    would leave the caches full of dirty lines whose write-back the next timed
+    kernel would pay for."""
+    import torch
+    buf = torch.ones(FLUSH_BYTES // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty((), dtype=torch.int32, device="cuda")
+    return lambda: torch.amax(buf, dim=0, out=sink)
+
+
+def blas_threads():
+    try:
+        from threadpoolctl import threadpool_info
+        return max([i.get("num_threads", 1) for i in threadpool_info() if i.get("user_api") == "blas"] or [1])
+    except Exception:  # pragma: no cover
+        return 1
+
+
+def bench_decode_sweep(args):
+    """Attention split + merge of the 8B-shaped decode layer at batch 1, 8, 64 and
+    256 (the first B sequences of one 256-sequence pool), MALL flushed before each
+    repetition, against the fastest split-K split count."""
+    torch, bi, synth = _torch_env()
+    from synth.workloads import build_decode_workload
+    cfg = bi.AttnConfig(HQ, HKV, D, page_size=P, split_size=S)
+    pool = synth.llama8b_decode_lengths(256, args.seed)
+    flush = mall_flusher()
+    reps = max(args.steps, 20)
+    props = torch.cuda.get_device_properties(0)
+    rows = []
+    for B in (1, 8, 64, 256):
+        wl = build_decode_workload(HQ, HKV, D, batch=B, seed=args.seed, lengths=pool[:B])
+        ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, B, wl.max_seq_len))
+        out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
+
+        def inv():
+            bi.bi_paged_attention_split(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                        wl.max_seq_len, ws)
+            bi.bi_paged_attention_merge(cfg, wl.seq_lens, wl.qsl, B, wl.max_seq_len, ws, out=out)
+        inv()
+        t_inv = pct(rep_times_ms(inv, reps, flush))
+        heur = bi.bi_splitk_attention_heuristic(cfg, B, wl.max_seq_len, props.multi_processor_count, 8)
+        per_n = {}
+        for n in sorted({heur, 1, 2, 4, 8, 16, 32}):
+            ws_k = bi.alloc_workspace(bi.bi_paged_attention_splitk_workspace_size(cfg, B, B, wl.max_seq_len, n))
+
+            def sk():
+                bi.bi_paged_attention_splitk(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                             wl.max_seq_len, n, workspace=ws_k, out=out)
+            sk()
+            per_n[n] = pct(rep_times_ms(sk, reps, flush))["median"]
+            del ws_k
+        best = min(per_n, key=per_n.get)
+        nbytes = split_bytes(wl.lengths) + B * HQ * D * 2
+        gbps = nbytes / (t_inv["median"] * 1e-3) / 1e9
+        rows.append({"batch": B, "algorithmic_bytes": nbytes, "invariant_ms": {k: round(v, 4) for k, v in t_inv.items()},
+                     "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
+                     "splitk_ms": round(per_n[best], 4), "splitk_num_splits": best, "heuristic_num_splits": heur,
+                     "overhead_vs_splitk": round(t_inv["median"] / per_n[best] - 1.0, 4)})
+        print(json.dumps({"progress": rows[-1]}), file=sys.stderr, flush=True)
+        del wl, ws
+        torch.cuda.empty_cache()
+    top = rows[-1]
+    print(json.dumps({
+        "metric": METRIC, "value": top["gbps"], "unit": "GB/s", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": top["invariant_ms"]["median"], "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "llama3.1-8b-shaped decode attention (split + merge), batch sweep, MALL flushed per rep",
+                   "q_heads": HQ, "kv_heads": HKV, "head_dim": D, "page_size": P, "split_size": S,
+                   "context_lengths": "U{512..8192}"},
+        "rows": rows}), flush=True)
+
+
+def bench_gemm(args):
+    """RMSNorm (hidden 4096) then the M-independent GEMM against [N, 4096] weights,
+    per (N, M); MALL flushed before each repetition.  Comparator: the fastest of
+    the split-K counts {1, 2, 4, 8, 16} whose fp32 partials fit in 2 GiB."""
+    torch, bi, synth = _torch_env()
+    K = 4096
+    reps = max(args.steps, 20)
+    flush = mall_flusher()
+    rows = []
+    cpu = None
+    for N, odt in ((14336, torch.bfloat16), (128256, torch.float32)):
+        W = synth.normal_bf16_device((N, K), args.seed + 40 + N % 7, std=0.02)
+        for M in (1, 7, 64, 256, 1024):
+            x = synth.normal_bf16_device((M, K), args.seed + 50 + M)
+            g = synth.normal_bf16_device((K,), args.seed + 49, std=0.1, mean=1.0)
+            xn = torch.empty_like(x)
+            c = torch.empty((M, N), dtype=odt, device="cuda")
+            rms = lambda: bi.bi_rmsnorm(x, g, 1e-5, out=xn)  # noqa: E731
+            gem = lambda: bi.bi_gemm(xn, W, out=c)  # noqa: E731
+            rms()
+            gem()
+            t_rms = pct(rep_times_ms(rms, reps, flush))
+            t_gemm = pct(rep_times_ms(gem, reps, flush))
+            per_k = {}
+            for ks in (1, 2, 4, 8, 16):
+                if K % (32 * ks) or M * N * 4 * ks > (2 << 30):
+                    continue
+                ws = torch.empty(M * N * ks, dtype=torch.float32, device="cuda")
+                c2 = torch.empty_like(c)
+                sk = lambda: bi.bi_gemm_splitk(xn, W, ks, out=c2, workspace=ws)  # noqa: E731
+                sk()
+                per_k[ks] = pct(rep_times_ms(sk, reps, flush))["median"]
+                del ws, c2
+            best = min(per_k, key=per_k.get)
+            flops = 2.0 * M * N * K
+            nbytes = 2 * M * K + 2 * N * K + (4 if odt == torch.float32 else 2) * M * N
+            t_mfma, t_hbm = flops / (PEAK_BF16_TFLOPS * 1e12), nbytes / (PEAK_HBM_GBPS * 1e9)
+            tm = t_gemm["median"] * 1e-3
+            rows.append({
+                "N": N, "M": M, "out": "fp32" if odt == torch.float32 else "bf16",
+                "rmsnorm_us": round(t_rms["median"] * 1e3, 2),
+                "rmsnorm_gbps": round((4 * M * K + 2 * K) / (t_rms["median"] * 1e-3) / 1e9, 1),
+                "gemm_us": {k: round(v * 1e3, 2) for k, v in t_gemm.items()},
+                "gemm_tflops": round(flops / tm / 1e12, 1), "gemm_gbps": round(nbytes / tm / 1e9, 1),
+                "bound": "mfma" if t_mfma > t_hbm else "hbm",
+                "roofline_us": round(max(t_mfma, t_hbm) * 1e6, 2),
+                "frac_of_roofline": round(max(t_mfma, t_hbm) / tm, 4),
+                "mfma_frac_of_bf16_peak": round(flops / tm / 1e12 / PEAK_BF16_TFLOPS, 4),
+                "splitk_us": round(per_k[best] * 1e3, 2), "splitk_k_splits": best,
+                "overhead_vs_splitk": round(t_gemm["median"] / per_k[best] - 1.0, 4)})
+            print(json.dumps({"progress": rows[-1]}), file=sys.stderr, flush=True)
+            del x, xn, c
+        if not args.no_cpu_baseline and N == 14336:
+            cpu = gemm_cpu_baseline(W, args.seed)
+        del W
+        torch.cuda.empty_cache()
+    head = [r for r in rows if r["N"] == 14336 and r["M"] == 256][0]
+    print(json.dumps({
+        "metric": "batch-invariant RMSNorm + GEMM: GEMM fraction of roofline", "value": head["frac_of_roofline"],
+        "unit": "fraction of min(bf16 MFMA peak, HBM) roofline", "n_gpus": 1, "steps": reps, "warmup": 1,
+        "ms_per_step": head["gemm_us"]["median"] / 1e3, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "rmsnorm + gemm, K 4096, M {1,7,64,256,1024} x N {14336 bf16, 128256 fp32}, "
+                               "MALL flushed per rep", "value_row": "N 14336, M 256"},
+        "rows": rows, "cpu_baseline": cpu}), flush=True)
+
+
+def gemm_cpu_baseline(W, seed):
+    """The oracle's RMSNorm + matmul (fp64 numpy) for M = 64 rows against the
+    [14336, 4096] weight, timed on the host."""
+    import oracle
+    import synth
+    x = synth.to_f64(synth.normal_bf16((64, W.shape[1]), seed + 77))
+    g = synth.to_f64(synth.normal_bf16((W.shape[1],), seed + 78, std=0.1, mean=1.0))
+    w = synth.to_f64(W.cpu())
+    t0 = time.perf_counter()
+    xn = oracle.rmsnorm_ref(x, g, 1e-5)
+    oracle.gemm_ref(xn, w)
+    dt = time.perf_counter() - t0
+    flops = 2.0 * 64 * W.shape[0] * W.shape[1]
+    return {"value": round(flops / dt / 1e9, 2), "unit": "GFLOP/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"float64 numpy rmsnorm + matmul, M 64 x N {W.shape[0]} x K {W.shape[1]}, {dt:.2f} s"}
+
+
+def prefill_schedule(unique, budget):
+    """Steps of a chunked prefill: request 0 computes the 1024-token prefix alone,
+    then every request continues from it (shared pages).  A step takes up to
+    `budget` tokens in request order; budget 0 means token by token (one row per
+    live request).  Each step is a list of (request, first position, tokens)."""
+    total = [1024 + u for u in unique]
+    steps = []
+    pos = 0
+    while pos < 1024:
+        n = 1 if budget == 0 else min(budget, 1024 - pos)
+        steps.append([(0, pos, n)])
+        pos += n
+    done = [1024] * len(unique)
+    while any(d < t for d, t in zip(done, total)):
+        st, left = [], budget
+        for r in range(len(unique)):
+            if done[r] >= total[r]:
+                continue
+            if budget == 0:
+                n = 1
+            else:
+                if left == 0:
+                    break
+                n = min(left, total[r] - done[r])
+                left -= n
+            st.append((r, done[r], n))
+            done[r] += n
+        steps.append(st)
+    return steps
+
+
+def bench_prefill(args):
+    """Attention (split + merge) over every step of a chunked-prefill schedule of
+    8 requests sharing a 1024-token prefix, each with U{256..2048} unique tokens.
+    The paged cache is filled beforehand; each schedule is captured as one HIP
+    graph and replayed."""
+    torch, bi, synth = _torch_env()
+    cfg = bi.AttnConfig(HQ, HKV, D, page_size=P, split_size=S)
+    nreq = 8
+    unique = synth.uniform_ints(nreq, 256, 2048, args.seed + 60)
+    total = [1024 + u for u in unique]
+    shared = synth.pages_needed(1024, P)
+    perm = synth.permutation(shared + sum(synth.pages_needed(u, P) for u in unique) + 16, args.seed + 61)
+    prefix_pages, cur = perm[:shared], shared
+    tables = []
+    for u in unique:
+        n = synth.pages_needed(u, P)
+        tables.append(prefix_pages + perm[cur:cur + n])
+        cur += n
+    num_pages = len(perm)
+    k_cache = synth.normal_bf16_device(cfg.k_cache_shape(num_pages), args.seed + 62)
+    v_cache = synth.normal_bf16_device(cfg.v_cache_shape(num_pages), args.seed + 63)
+    q_all = synth.normal_bf16_device((1024 + max(total), HQ, D), args.seed + 64)
+    stride = max(len(t) for t in tables)
+    flush = mall_flusher()
+    rows = []
+    for budget in (16, 128, 512, 0):
+        steps = prefill_schedule(unique, budget)
+        meta = []
+        max_ws = 0
+        for st in steps:
+            pt = torch.tensor([tables[r] + [-1] * (stride - len(tables[r])) for r, _, _ in st], dtype=torch.int32)
+            sl = [s0 + n for _, s0, n in st]
+            ql = [n for _, _, n in st]
+            T = sum(ql)
+            qsl = [0]
+            for n in ql:
+                qsl.append(qsl[-1] + n)
+            meta.append((pt.cuda(), torch.tensor(sl, dtype=torch.int32, device="cuda"),
+                         torch.tensor(qsl, dtype=torch.int32, device="cuda"), T, max(sl), q_all[:T]))
+            max_ws = max(max_ws, bi.bi_paged_attention_workspace_size(cfg, len(st), T, max(sl)))
+        ws = bi.alloc_workspace(max_ws)
+        outs = [torch.empty((m[3], HQ, D), dtype=torch.bfloat16, device="cuda") for m in meta]
+
+        def run_all():
+            for (pt, sl, qsl, T, msl, q), o in zip(meta, outs):
+                bi.bi_paged_attention(cfg, q, k_cache, v_cache, pt, sl, qsl, msl, workspace=ws, out=o)
+        run_all()
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            run_all()
+        graph.replay()
+        torch.cuda.synchronize()
+        t = pct(rep_times_ms(graph.replay, max(3, min(args.steps, 10)), flush))
+        flops = 0
+        kv_bytes = 0
+        tokens = 0
+        for st in steps:
+            for _, s0, n in st:
+                tokens += n
+                flops += sum(4 * D * HQ * (s0 + j + 1) for j in range(n))
+                kv_bytes += 2 * (s0 + n) * HKV * D * 2
+        sec = t["median"] * 1e-3
+        rows.append({"budget": budget or "token-by-token", "steps": len(steps), "tokens": tokens,
+                     "ms": {k: round(v, 3) for k, v in t.items()}, "tokens_per_s": round(tokens / sec, 1),
+                     "tflops": round(flops / sec / 1e12, 2), "mfma_frac_of_bf16_peak": round(flops / sec / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "kv_gbps": round(kv_bytes / sec / 1e9, 1), "algorithmic_flops": flops, "kv_bytes": kv_bytes})
+        print(json.dumps({"progress": rows[-1]}), file=sys.stderr, flush=True)
+        del graph, meta, outs, ws
+        torch.cuda.empty_cache()
+    head = [r for r in rows if r["budget"] == 512][0]
+    print(json.dumps({
+        "metric": "batch-invariant chunked prefill attention tokens/s", "value": head["tokens_per_s"],
+        "unit": "tokens/s", "n_gpus": 1, "steps": len(rows), "warmup": 1, "ms_per_step": head["ms"]["median"],
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "8 requests, shared 1024-token prefix + U{256..2048} unique tokens, llama3.1-8b-shaped "
+                               "attention layer, chunk budgets {16,128,512} and token by token",
+                   "unique_tokens": unique, "value_row": "budget 512"},
+        "rows": rows}), flush=True)
+
+
+def bench_gemma(args):
+    """One decode step (one new token per sequence) of the 34-layer Gemma-3-4B-shaped
+    decoder over a paged cache, captured as one HIP graph and replayed."""
+    torch, bi, synth = _torch_env()
+    from deterministic_paged_attention_amd.decoder import Decoder, DecoderShape
+    from synth.workloads import decoder_weights
+    s = DecoderShape()
+    B = args.batch
+    ctx = synth.uniform_ints(B, 512, 4096, args.seed + 70)
+    w = decoder_weights(s.layers, s.hidden, s.q_heads, s.kv_heads, s.head_dim, s.ffn, s.vocab, seed=args.seed + 71)
+    dec = Decoder(s, w)
+    k_lens = [L + 1 for L in ctx]
+    need = [synth.pages_needed(L, s.page_size) for L in k_lens]
+    num_pages = sum(need) + 16
+    perm = synth.permutation(num_pages, args.seed + 72)
+    tables, cur = [], 0
+    for n in need:
+        tables.append(perm[cur:cur + n])
+        cur += n
+    stride = max(need)
+    pt = torch.tensor([t + [-1] * (stride - len(t)) for t in tables], dtype=torch.int32, device="cuda")
+    caches = dec.new_caches(num_pages)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(args.seed + 73)
+    for k, v in caches:
+        k.normal_(generator=g)
+        v.normal_(generator=g)
+    ids = torch.tensor(synth.uniform_ints(B, 0, s.vocab - 1, args.seed + 74), dtype=torch.int32, device="cuda")
+    sl = torch.tensor(k_lens, dtype=torch.int32, device="cuda")
+    qsl = torch.arange(B + 1, dtype=torch.int32, device="cuda")
+    step = lambda: dec.step(ids, caches, pt, sl, qsl, max(k_lens))  # noqa: E731
+    for _ in range(2):
+        step()
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        logits = step()
+    for _ in range(max(1, args.warmup)):
+        graph.replay()
+    torch.cuda.synchronize()
+    ts = rep_times_ms(graph.replay, args.steps)
+    t = pct(ts)
+    eager = pct(rep_times_ms(step, 3))
+    per_layer = s.qkv_width * s.hidden + s.hidden * s.q_heads * s.head_dim + 2 * s.ffn * s.hidden + s.hidden * s.ffn
+    n_global = sum(1 for l in range(s.layers) if s.is_global(l))
+    n_local = s.layers - n_global
+    w_bytes = 2 * (s.layers * per_layer + s.vocab * s.hidden)
+    kv_token = 2 * s.kv_heads * s.head_dim * 2
+    kv_read = sum(kv_token * (n_local * min(L, s.window) + n_global * L) for L in k_lens)
+    kv_write = s.layers * B * kv_token
+    logits_bytes = B * s.vocab * 4
+    nbytes = w_bytes + kv_read + kv_write + logits_bytes
+    sec = t["median"] * 1e-3
+    cpu = None if args.no_cpu_baseline else gemma_cpu_baseline(dec, ctx[0], args.seed)
+    print(json.dumps({
+        "metric": "batch-invariant decoder decode step: tokens/s", "value": round(B / sec, 1), "unit": "tokens/s",
+        "n_gpus": 1, "steps": args.steps, "warmup": args.warmup, "ms_per_step": round(t["median"], 4),
+        "higher_is_better": True, "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "gemma-3-4b-shaped decoder (random init), one decode token per sequence, HIP graph",
+                   "batch": B, "context_lengths": "U{512..4096}", "mean_context": round(sum(ctx) / B, 1),
+                   "layers": s.layers, "hidden": s.hidden, "q_heads": s.q_heads, "kv_heads": s.kv_heads,
+                   "head_dim": s.head_dim, "ffn": s.ffn, "vocab": s.vocab, "window": s.window,
+                   "global_layers": n_global},
+        "step_ms": {k: round(v, 4) for k, v in t.items()}, "eager_step_ms": round(eager["median"], 4),
+        "roofline": {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                     "frac": round(nbytes / sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
+                     "algorithmic_bytes_per_step": nbytes, "weight_bytes": w_bytes, "kv_read_bytes": kv_read},
+        "logits_shape": list(logits.shape), "cpu_baseline": cpu}), flush=True)
+
+
+def gemma_cpu_baseline(dec, ctx_len, seed):
+    """The oracle's per-op chain for one layer (layer 0, local) at batch 1 with a
+    context of ctx_len tokens (fp64 numpy), timed on the host."""
+    import numpy as np
+    import oracle
+    import synth
+    s = dec.shape
+    W = {k: synth.to_f64(v.cpu()) for k, v in dec.w["layers"][0].items()}
+    L = ctx_len + 1
+    h = synth.to_f64(synth.normal_bf16((1, s.hidden), seed + 80))
+    kc = synth.to_f64(synth.normal_bf16((synth.pages_needed(L, s.page_size), s.page_size, s.kv_heads, s.head_dim),
+                                        seed + 81))
+    vc = synth.to_f64(synth.normal_bf16(kc.shape, seed + 82))
+    Hq, Hk, D = s.q_heads, s.kv_heads, s.head_dim
+    t0 = time.perf_counter()
+    xn = oracle.rmsnorm_ref(h, W["g_attn"], s.eps)
+    qkv = oracle.gemm_ref(xn, W["w_qkv"])
+    q, k = oracle.qk_norm_rope_ref(qkv[:, :Hq * D].reshape(1, Hq, D), qkv[:, Hq * D:(Hq + Hk) * D].reshape(1, Hk, D),
+                                   W["g_q"], W["g_k"], s.eps, [L - 1], s.theta_local)
+    table = np.arange(kc.shape[0])[None, :]
+    o = oracle.attention_ref(q, kc, vc, table, [L], [0, 1], Hk, s.page_size, window=s.window)
+    h2 = oracle.add_ref(h, oracle.gemm_ref(o.reshape(1, -1), W["w_o"]))
+    gu = oracle.gemm_ref(oracle.rmsnorm_ref(h2, W["g_mlp"], s.eps), W["w_gu"])
+    oracle.add_ref(h2, oracle.gemm_ref(oracle.gated_gelu_ref(gu), W["w_down"]))
+    dt = time.perf_counter() - t0
+    per_layer = sum(int(np.prod(v.shape)) for v in W.values()) * 2 + 2 * min(L, s.window) * Hk * D * 2
+    return {"value": round(per_layer / dt / 1e9, 3), "unit": "GB/s", "cores": blas_threads(), "kind": "oracle",
+            "sample": f"float64 numpy per-op chain of one local layer at batch 1, context {L}: {dt:.3f} s "
+                      f"(bf16-equivalent bytes of that layer / time)"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="decode", choices=["decode", "decode-sweep", "gemm", "prefill", "gemma"])
+    ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--seed", type=int, default=2000)
+    ap.add_argument("--cpu-sample", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-splitk", action="store_true")
+    ap.add_argument("--copy-calibration-mib", type=int, default=0,
+                    help="also run one plain device copy of this size (for HBM counter calibration)")
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only: the method is single-GPU and this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
+        sys.exit(2)
+    {"decode": bench_decode, "decode-sweep": bench_decode_sweep, "gemm": bench_gemm, "prefill": bench_prefill,
+     "gemma": bench_gemma}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -430,6 +430,8 @@ bi_status check_gemm(const void* a, int64_t lda, const void* w, int64_t ldw, con
   if (lda < K || ldw < K || ldc < N || lda % 8 || ldw % 8)
     return fail(BI_ERR_INVALID_ARG, "lda, ldw must be >= K and multiples of 8; ldc >= N");
   if ((M + 15) / 16 > 65535 || N > 0x7fffffffLL) return fail(BI_ERR_OUT_OF_RANGE, "M or N too large");
+  // Each workgroup addresses at most 256 rows of a or w through 32-bit byte offsets.
+  if (lda >= (1LL << 23) || ldw >= (1LL << 23)) return fail(BI_ERR_OUT_OF_RANGE, "lda, ldw must be below 2^23");
   if (M == 0 || N == 0) return BI_OK;
   if (!a || !w || !c) return fail(BI_ERR_INVALID_ARG, "null device pointer");
   if (!aligned(a, 16) || !aligned(w, 16)) return fail(BI_ERR_INVALID_ARG, "a and w must be 16-byte aligned");

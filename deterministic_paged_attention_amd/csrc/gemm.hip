@@ -8,25 +8,25 @@
 // per 32-wide K step, in increasing K order — the same instruction sequence
 // whatever M is and wherever the row sits in its tile.  There is no split of K.
 //
-// Mapping: one wave owns a 16 (n) x 16 (m) output block and computes C^T =
-// W A^T, so that a lane ends with four consecutive n of one m (one vector
-// store).  A operand = 16 rows of w, B operand = 16 rows of a; both are read
-// straight from global memory as 16-byte runs along K (K-major storage).
+// Fragments: an output block is 16 (n) x 16 (m); a wave computes C^T = W A^T
+// for it, so that a lane ends with four consecutive n of one m (one vector
+// store).  The MFMA A operand is 16 rows of w, the B operand 16 rows of a;
+// lane l supplies k-slots 8*(l>>4) .. 8*(l>>4)+7 of the 32-wide K step, both
+// operands K-major as stored.
 //
 // Two work mappings share that per-element arithmetic exactly (same
 // instruction, same K steps in the same order, same k-slot layout per lane
 // group), so which one runs never changes a bit of any output row:
-//  * gemm_kernel (M <= 32): one wave per 16 (n) x 16 (m) block, operands read
-//    straight from global memory — weight streaming for decode-sized M;
-//  * gemm_tiled_kernel<BM, BN> (larger M): a workgroup owns a BM x BN tile,
-//    stages 64-wide K slices of both operands through LDS (double-buffered),
-//    and each of its four waves computes a (BM/2) x (BN/2) sub-tile; tiles are
-//    ordered so that the workgroups sharing a slice of w run on one XCD (one
-//    L2).
-//
-// The split-K comparator (measurement only) runs gemm_kernel over K
-// sub-ranges into fp32 partials and sums them in split order afterwards, so
-// its reduction order follows the number of splits.
+//  * gemm_ring_kernel<BM, BN, WM, BK, STAGES> (the product path, every M): a
+//    workgroup owns a BM x BN tile and streams BK-wide K slices of both
+//    operands into an LDS ring with direct-to-LDS buffer loads; the tile
+//    configuration is chosen from M and N;
+//  * gemm_kernel: one wave per block, operands read straight from global
+//    memory into registers.  It serves the split-K comparator (measurement
+//    only), which runs it over K sub-ranges into fp32 partials and sums them in
+//    split order afterwards, so that reduction order follows the number of
+//    splits.  Run with one split it performs the product's arithmetic, which
+//    makes it a cross-check of the ring mapping.
 
 #include "bi_internal.h"
 
@@ -111,28 +111,91 @@ __global__ __launch_bounds__(64 * kWaves) void gemm_kernel(const uint16_t* a, in
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled mapping.
+// LDS ring mapping.
+//
+// A workgroup (four waves) owns a BM x BN output tile.  K is consumed in
+// BK-wide slices; slice s of both operands is copied straight from global
+// memory into LDS stage s % STAGES by buffer loads that write LDS directly
+// (each wave instruction moves 1 KiB: 512/BK rows x 2*BK bytes; lane i of it
+// writes the i-th 16-byte LDS slot).  STAGES - 1 slices are in flight while one is being
+// multiplied, which is what keeps HBM busy when there are few workgroups per
+// CU (skinny M) and the K loop is long.  Rows past M or N are fetched through
+// a buffer descriptor whose range ends at the last valid element, so they
+// arrive as zeros without touching memory.
+//
+// LDS layout of one operand slice: row-major, BK/8 chunks of 16 bytes per
+// row, chunk c of row R stored at slot R*BK/8 + (c ^ (R & 7)), so that the
+// 8 rows a group of fragment-reading lanes touches fall in distinct banks.
 // ---------------------------------------------------------------------------
-constexpr int kBK = 64;          // K slice staged per iteration (two MFMA K steps)
-constexpr int kLdsRow = kBK + 8; // padded LDS row (elements): conflict-free fragment reads
 constexpr int kXcds = 8;         // workgroups are dispatched round-robin over 8 XCDs
 
-template <int BM, int BN>
-__global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
-                                                         int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
-                                                         int64_t N, int64_t K) {
-  constexpr int MB = BM / 32;                 // 16-row m blocks per wave
-  constexpr int NB = BN / 32;                 // 16-row n blocks per wave
-  constexpr int A_CHUNKS = BM * (kBK / 8) / 256;  // 16-byte chunks per thread per slice
-  constexpr int W_CHUNKS = BN * (kBK / 8) / 256;
-  __shared__ __attribute__((aligned(16))) uint16_t lds_a[2][BM * kLdsRow];
-  __shared__ __attribute__((aligned(16))) uint16_t lds_w[2][BN * kLdsRow];
+// s_waitcnt with vmcnt = n and the other counters left free (gfx9 encoding:
+// vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]).
+template <int n>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
 
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
+typedef __attribute__((address_space(3))) void lds_void;
+
+// 16-byte LDS read at byte address addr (result valid after lds_wait).  The
+// bodies are GPU assembly; the host pass of the compiler only sees stubs.
+__device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
+  u32x4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+#else
+  v = u32x4{addr, 0u, 0u, 0u};
+#endif
+  return v;
+}
+
+// Waits for every outstanding LDS read of this wave; the fragments are tied
+// to the wait so no use of them can be scheduled above it.
+template <int NA, int NB>
+__device__ __forceinline__ void lds_wait(u32x4 (&x)[NA], u32x4 (&y)[NB]) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int i = 0; i < NA; ++i) asm volatile("" : "+v"(x[i]));
+#pragma unroll
+  for (int i = 0; i < NB; ++i) asm volatile("" : "+v"(y[i]));
+#endif
+}
+
+// Buffer descriptor over `rows` rows (ld elements apart) of K valid elements
+// starting at base; everything past the last valid element reads as zero.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base, int64_t rows, int64_t ld,
+                                                            int64_t K) {
+  const int64_t bytes = rows > 0 ? ((rows - 1) * ld + K) * 2 : 0;
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<uint16_t*>(base), (short)0, (int)(uint32_t)bytes,
+                                           0x00020000);
+}
+
+template <int BM, int BN, int WM, int BK, int STAGES>
+__global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
+                                                        int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
+                                                        int64_t N, int64_t K) {
+#if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts and buffer-to-LDS copies exist on the GPU only
+  constexpr int WN = 4 / WM;
+  constexpr int MB = BM / WM / 16;            // 16-row m blocks per wave
+  constexpr int NB = BN / WN / 16;            // 16-row n blocks per wave
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per row of a slice
+  constexpr int RPI = 64 / CPR;               // rows moved by one copy instruction
+  constexpr int G = (BM + BN) / RPI;          // copy instructions per slice
+  constexpr int IPW = (G + 3) / 4;            // per slice for waves 0 .. G%4-1 (all if G%4 == 0)
+  constexpr int STAGE = (BM + BN) * BK;       // elements per stage
+  constexpr int SPS = BK / 32;                // MFMA K steps per slice
+  static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "tile shape");
+  static_assert((BK == 64 || BK == 128 || BK == 256 || BK == 512) && (BM + BN) % RPI == 0, "slice shape");
+  static_assert(STAGES >= 2, "ring depth");
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
+
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int r = lane & 15, g4 = lane >> 4;
-  const int wm = wave & 1, wn = wave >> 1;
+  const int wm = wave % WM, wn = wave / WM;
 
   // XCD-aware tile order: workgroup ids id and id + 8 share an XCD; each XCD
   // gets a contiguous run of tiles, m fastest, so the m tiles that read the
@@ -144,36 +207,38 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* a, int6
   const int64_t m0 = (tile % nM) * BM;
   const int64_t n0 = (tile / nM) * BN;
 
-  // Global -> register staging of one K slice.
-  u32x4 ra[A_CHUNKS], rw[W_CHUNKS];
-  auto load_slice = [&](int64_t k0) {
+  // Copy plan: instruction j of this wave moves rows RPI*gi .. RPI*gi+RPI-1
+  // of the stacked [a rows; w rows] slice, gi = wave + 4j, if gi < G.
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(a + m0 * lda, min<int64_t>(BM, M - m0), lda, K);
+  const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w + n0 * ldw, min<int64_t>(BN, N - n0), ldw, K);
+  const __amdgpu_buffer_rsrc_t rzero = rows_rsrc(a, 0, lda, K);
+  uint32_t voff[IPW];
+  __amdgpu_buffer_rsrc_t rsj[IPW];
 #pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, col = (ch & 7) * 8;
-      const int64_t m = m0 + row;
-      ra[i] = (m < M && k0 + col < K) ? *reinterpret_cast<const u32x4*>(a + m * lda + k0 + col)
-                                      : u32x4{0u, 0u, 0u, 0u};
-    }
+  for (int j = 0; j < IPW; ++j) {
+    const int srow = RPI * (wave + 4 * j) + lane / CPR;    // row of the stacked slice
+    const bool is_a = srow < BM;
+    const int row = is_a ? srow : srow - BM;
+    const int chunk = (lane % CPR) ^ (srow & 7);           // logical chunk landing in this lane's slot
+    voff[j] = (uint32_t)(row * (is_a ? lda : ldw) * 2 + chunk * 16);
+    rsj[j] = is_a ? ra : rw;
+  }
+  const int64_t nsteps = K / 32;
+  const int64_t nslices = (nsteps + SPS - 1) / SPS;
+  // Slice s into stage s % STAGES; slices past the end copy nothing (a
+  // zero-range descriptor) so that every iteration issues the same count.
+  auto issue = [&](int64_t s) {
+    const int st = (int)(s % STAGES);
+    const bool live = s < nslices;
 #pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, col = (ch & 7) * 8;
-      const int64_t n = n0 + row;
-      rw[i] = (n < N && k0 + col < K) ? *reinterpret_cast<const u32x4*>(w + n * ldw + k0 + col)
-                                      : u32x4{0u, 0u, 0u, 0u};
+    for (int j = 0; j < IPW; ++j) {
+      if (wave + 4 * j >= G) break;          // wave-uniform
+      lds_void* dst = (lds_void*)(lds + st * STAGE + (wave + 4 * j) * 512);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsj[j] : rzero, dst, 16,
+                                               voff[j] + (uint32_t)(s * BK * 2), 0, 0, 0);
     }
   };
-  auto store_slice = [&](int buf) {
-#pragma unroll
-    for (int i = 0; i < A_CHUNKS; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, col = (ch & 7) * 8;
-      *reinterpret_cast<u32x4*>(&lds_a[buf][row * kLdsRow + col]) = ra[i];
-    }
-#pragma unroll
-    for (int i = 0; i < W_CHUNKS; ++i) {
-      const int ch = tid + 256 * i, row = ch >> 3, col = (ch & 7) * 8;
-      *reinterpret_cast<u32x4*>(&lds_w[buf][row * kLdsRow + col]) = rw[i];
-    }
-  };
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
 
   f32x4 acc[NB][MB];
 #pragma unroll
@@ -181,40 +246,48 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* a, int6
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  const int64_t nsteps = K / 32;              // MFMA K steps in total
-  const int64_t nslices = (nsteps + 1) / 2;
-  load_slice(0);
-  store_slice(0);
-  __syncthreads();
-  for (int64_t sl = 0; sl < nslices; ++sl) {
-    const int buf = (int)(sl & 1);
-    if (sl + 1 < nslices) load_slice((sl + 1) * kBK);
-    const int ksteps = (int)min<int64_t>(2, nsteps - 2 * sl);  // 1 only on an odd final slice
+#pragma unroll
+  for (int p = 0; p < STAGES - 1; ++p) issue(p);
+  for (int64_t s = 0; s < nslices; ++s) {
+    // The copies land in LDS behind the compiler's back, so the fragment
+    // reads below are explicit ds_read instructions and the waits are ours:
+    // this wave's copies of slice s are done (vmcnt), then everyone's are and
+    // nobody still reads slice s-1 (barrier).
+    if (G % 4 == 0 || wave < G % 4) wait_vmcnt<IPW * (STAGES - 2)>();
+    else wait_vmcnt<(IPW - 1) * (STAGES - 2)>();
+    __builtin_amdgcn_s_barrier();
+    issue(s + STAGES - 1);                   // into the stage slice s-1 used
+    const uint32_t sa = lds_base + (uint32_t)((s % STAGES) * STAGE * 2);
+    const uint32_t sw = sa + BM * BK * 2;
+    const int ksteps = (int)min<int64_t>(SPS, nsteps - SPS * s);  // fewer only on a ragged final slice
     for (int ks = 0; ks < ksteps; ++ks) {
-      bf16x8 fw[NB], fa[MB];
+      const uint32_t cs = (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16);
+      u32x4 fw[NB], fa[MB];
 #pragma unroll
       for (int i = 0; i < NB; ++i)
-        fw[i] = *reinterpret_cast<const bf16x8*>(&lds_w[buf][(wn * (BN / 2) + 16 * i + r) * kLdsRow + ks * 32 + 8 * g4]);
+        fw[i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
 #pragma unroll
       for (int j = 0; j < MB; ++j)
-        fa[j] = *reinterpret_cast<const bf16x8*>(&lds_a[buf][(wm * (BM / 2) + 16 * j + r) * kLdsRow + ks * 32 + 8 * g4]);
+        fa[j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
+      lds_wait(fw, fa);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
-        for (int j = 0; j < MB; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fw[i], fa[j], acc[i][j], 0, 0, 0);
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[i]),
+                                                             __builtin_bit_cast(bf16x8, fa[j]), acc[i][j], 0, 0, 0);
     }
-    if (sl + 1 < nslices) store_slice(buf ^ 1);
-    __syncthreads();
   }
+  wait_vmcnt<0>();                           // drain the trailing (empty) copies
 
   // Lane holds C^T[n + 4*g4 + i][m + r] of each block.
 #pragma unroll
   for (int j = 0; j < MB; ++j) {
-    const int64_t m = m0 + wm * (BM / 2) + 16 * j + r;
+    const int64_t m = m0 + wm * (BM / WM) + 16 * j + r;
     if (m >= M) continue;
 #pragma unroll
     for (int i = 0; i < NB; ++i) {
-      const int64_t nb = n0 + wn * (BN / 2) + 16 * i + 4 * g4;
+      const int64_t nb = n0 + wn * (BN / WN) + 16 * i + 4 * g4;
       if (out_kind == 1) {
         float* cp = reinterpret_cast<float*>(c) + m * ldc + nb;
         if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 15) == 0)) {
@@ -238,15 +311,16 @@ __global__ __launch_bounds__(256) void gemm_tiled_kernel(const uint16_t* a, int6
       }
     }
   }
+#endif
 }
 
-template <int BM, int BN>
-hipError_t tiled_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
-                        int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+template <int BM, int BN, int WM, int BK, int STAGES>
+hipError_t ring_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
+                       int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t groups = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_tiled_kernel<BM, BN>), dim3((unsigned)groups), dim3(256), 0, stream, a, lda, w, ldw, c,
-                     ldc, out_kind, M, N, K);
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, BK, STAGES>), dim3((unsigned)groups), dim3(256), 0, stream, a, lda,
+                     w, ldw, c, ldc, out_kind, M, N, K);
   return hipGetLastError();
 }
 
@@ -267,13 +341,33 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
 hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
                        int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  // The mapping follows M; the arithmetic of every output element does not.
-  if (M > 512) return tiled_launch<128, 128>(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream);
-  if (M > 32) return tiled_launch<64, 64>(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream);
-  dim3 grid((unsigned)((N + 16 * kWaves - 1) / (16 * kWaves)), (unsigned)((M + 15) / 16), 1);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(64 * kWaves), 0, stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K,
-                     (int64_t)0);
-  return hipGetLastError();
+  // The mapping follows M (and N, which every call of a given weight
+  // shares); the arithmetic of every output element does not.  Tile shape,
+  // slice width and ring depth come from a measured sweep on MI355X: skinny
+  // M wants long contiguous row runs and many slices in flight; larger M
+  // wants larger tiles to cut operand re-reads.
+  auto L = [&](auto kernel_cfg) { return kernel_cfg(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream); };
+  if (M <= 32) {
+    if (N >= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
+    return L(ring_launch<32, 32, 2, 512, 2>);
+  }
+  if (M <= 64) {
+    if (N >= 16384) return L(ring_launch<64, 128, 2, 128, 3>);
+    if (N >= 8192) return L(ring_launch<64, 64, 2, 128, 4>);
+    return L(ring_launch<32, 32, 2, 256, 4>);
+  }
+  if (M <= 128) {
+    if (N >= 16384) return L(ring_launch<128, 128, 2, 64, 4>);
+    if (N >= 8192) return L(ring_launch<64, 64, 2, 128, 2>);
+    return L(ring_launch<32, 32, 2, 256, 2>);
+  }
+  if (M <= 256) {
+    if (N >= 16384) return L(ring_launch<256, 128, 4, 64, 3>);
+    if (N >= 8192) return L(ring_launch<128, 128, 2, 64, 4>);
+    return L(ring_launch<64, 64, 2, 128, 4>);
+  }
+  if (N >= 8192) return L(ring_launch<256, 128, 4, 64, 3>);
+  return L(ring_launch<128, 128, 2, 64, 4>);
 }
 
 hipError_t launch_gemm_splitk(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, float* partial,

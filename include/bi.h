@@ -202,7 +202,9 @@ bi_status bi_rmsnorm(const void* x_dev, int64_t ld_x, const void* gamma_dev, flo
 /* a bf16 [M][K] (row stride lda), w bf16 [N][K] (row stride ldw), c [M][N]  */
 /* (row stride ldc) in bf16 or fp32.  bf16 MFMA, fp32 accumulation in one    */
 /* accumulator per output element, K visited in increasing 32-wide steps, no */
-/* split of K.  K must be a multiple of 32; lda, ldw multiples of 8.         */
+/* split of K.  K must be a multiple of 32; lda, ldw multiples of 8 and     */
+/* below 2^23 (BI_ERR_OUT_OF_RANGE otherwise).  The result does not depend   */
+/* on M, on the row's position, or on the tile configuration chosen.         */
 /* ------------------------------------------------------------------------ */
 bi_status bi_gemm(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw,
                   void* c_dev, int64_t ldc, bi_dtype c_dtype,

@@ -13,7 +13,8 @@ import torch
 import deterministic_paged_attention_amd as bi
 import oracle
 import synth
-from harness import (DEV, PagedKV, Request, logical_k, logical_v, nan_cache, oracle_rows, page_table_tensor,
+from harness import (DEV, PagedKV, Request, first_mismatch, logical_k, logical_v, nan_cache, oracle_rows,
+                     page_table_tensor,
                      run_step)
 
 pytestmark = pytest.mark.gpu
@@ -241,6 +242,36 @@ def test_gemm_parity(M, N):
     bound = oracle.gemm_abs_ref(synth.to_f64(a), synth.to_f64(w))
     assert np.all(np.abs(c32 - ref) <= 1e-3 * bound)
     assert np.max(np.abs(c16 - ref)) <= BF16_TOL
+
+
+@pytest.mark.parametrize("M", [1, 33, 129, 300])
+@pytest.mark.parametrize("K", [96, 4128])
+def test_gemm_ragged_k_tails_and_strides(M, K):
+    """K with an odd number of 32-wide steps (a half-empty last 64-wide slice),
+    M and N off every tile size, and row strides larger than K."""
+    N = 77
+    a = synth.normal_bf16((M, K + 24), 531)
+    w = synth.normal_bf16((N, K + 40), 532, std=0.02)
+    ad, wd = a.to(DEV)[:, :K], w.to(DEV)[:, :K]
+    out = torch.full((M, N + 5), 7.0, dtype=torch.float32, device=DEV)
+    bi.bi_gemm(ad, wd, out=out[:, :N])
+    ref = oracle.gemm_ref(synth.to_f64(a[:, :K]), synth.to_f64(w[:, :K]))
+    bound = oracle.gemm_abs_ref(synth.to_f64(a[:, :K]), synth.to_f64(w[:, :K]))
+    got = out.cpu().double().numpy()
+    assert np.all(np.abs(got[:, :N] - ref) <= 1e-3 * bound)
+    assert np.all(got[:, N:] == 7.0)
+
+
+@pytest.mark.parametrize("M", [1, 16, 17, 33, 65, 129, 300])
+def test_gemm_tile_mappings_agree_bitwise(M):
+    """The LDS-ring mapping (tile shape chosen from M) and the register-direct
+    mapping of the split-K comparator run with one split perform the same
+    per-element instruction sequence, so their fp32 outputs agree bit for bit."""
+    a = synth.normal_bf16_device((M, 2048), 541)
+    w = synth.normal_bf16_device((1000, 2048), 542, std=0.02)
+    ring = bi.bi_gemm(a, w, out_dtype=torch.float32)
+    direct = bi.bi_gemm_splitk(a, w, 1, out_dtype=torch.float32)
+    assert first_mismatch(ring, direct) is None
 
 
 def test_gemm_lm_head_full_size_sampled():
