@@ -14,19 +14,17 @@
 // lane l supplies k-slots 8*(l>>4) .. 8*(l>>4)+7 of the 32-wide K step, both
 // operands K-major as stored.
 //
-// Two work mappings share that per-element arithmetic exactly (same
-// instruction, same K steps in the same order, same k-slot layout per lane
-// group), so which one runs never changes a bit of any output row:
-//  * gemm_ring_kernel<BM, BN, WM, BK, STAGES> (the product path, every M): a
-//    workgroup owns a BM x BN tile and streams BK-wide K slices of both
-//    operands into an LDS ring with direct-to-LDS buffer loads; the tile
-//    configuration is chosen from M and N;
-//  * gemm_kernel: one wave per block, operands read straight from global
-//    memory into registers.  It serves the split-K comparator (measurement
-//    only), which runs it over K sub-ranges into fp32 partials and sums them in
-//    split order afterwards, so that reduction order follows the number of
-//    splits.  Run with one split it performs the product's arithmetic, which
-//    makes it a cross-check of the ring mapping.
+// The product mapping, gemm_ring_kernel<BM, BN, WM, BK, STAGES>: a workgroup
+// owns a BM x BN tile and streams BK-wide K slices of both operands into an
+// LDS ring with direct-to-LDS buffer loads.  The tile configuration is chosen
+// from M and N; every configuration performs the same per-element instruction
+// sequence (same instruction, same K steps in the same order, same k-slot
+// layout per lane group), so which one runs never changes a bit of any
+// output row.
+//
+// The split-K comparator (measurement only) runs the same kernel over K
+// sub-ranges into fp32 partials and sums them in split order afterwards, so
+// its reduction order follows the number of splits.
 
 #include "bi_internal.h"
 
@@ -38,77 +36,6 @@ typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-
-constexpr int kWaves = 4;    // waves per workgroup, side by side along n
-constexpr int kUnroll = 8;   // K steps whose operands are loaded together
-
-// out_kind: 0 = bf16 c, 1 = fp32 c.  K range [k_begin, k_begin + k_count).
-__global__ __launch_bounds__(64 * kWaves) void gemm_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
-                                                           int64_t ldw, void* c, int64_t ldc, int out_kind,
-                                                           int64_t M, int64_t N, int64_t k_count,
-                                                           int64_t split_stride_elems) {
-  const int lane = threadIdx.x & 63;
-  const int wave = threadIdx.x >> 6;
-  const int r = lane & 15;
-  const int g4 = lane >> 4;
-  const int64_t n0 = ((int64_t)blockIdx.x * kWaves + wave) * 16;
-  const int64_t m0 = (int64_t)blockIdx.y * 16;
-  if (n0 >= N) return;
-  const int64_t k_begin = (int64_t)blockIdx.z * k_count;
-
-  const bool n_ok = n0 + r < N;
-  const bool m_ok = m0 + r < M;
-  const uint16_t* wp = w + (n_ok ? (n0 + r) : 0) * ldw + k_begin + 8 * g4;
-  const uint16_t* ap = a + (m_ok ? (m0 + r) : 0) * lda + k_begin + 8 * g4;
-
-  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-  const int64_t nsteps = k_count / 32;
-  int64_t st = 0;
-  for (; st + kUnroll <= nsteps; st += kUnroll) {
-    u32x4 wf[kUnroll], af[kUnroll];
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u) {
-      wf[u] = n_ok ? *reinterpret_cast<const u32x4*>(wp + (st + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-      af[u] = m_ok ? *reinterpret_cast<const u32x4*>(ap + (st + u) * 32) : u32x4{0u, 0u, 0u, 0u};
-    }
-#pragma unroll
-    for (int u = 0; u < kUnroll; ++u)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf[u]),
-                                                    __builtin_bit_cast(bf16x8, af[u]), acc, 0, 0, 0);
-  }
-  for (; st < nsteps; ++st) {
-    const u32x4 wf = n_ok ? *reinterpret_cast<const u32x4*>(wp + st * 32) : u32x4{0u, 0u, 0u, 0u};
-    const u32x4 af = m_ok ? *reinterpret_cast<const u32x4*>(ap + st * 32) : u32x4{0u, 0u, 0u, 0u};
-    acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, wf), __builtin_bit_cast(bf16x8, af),
-                                                  acc, 0, 0, 0);
-  }
-
-  // Lane holds C^T[n0 + 4*g4 + i][m0 + r], i = 0..3.
-  if (!m_ok) return;
-  const int64_t m = m0 + r;
-  const int64_t nb = n0 + 4 * g4;
-  if (out_kind == 1) {
-    float* cp = reinterpret_cast<float*>(c) + (int64_t)blockIdx.z * split_stride_elems + m * ldc + nb;
-    if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 15) == 0)) {
-      *reinterpret_cast<f32x4*>(cp) = acc;
-    } else {
-      for (int i = 0; i < 4; ++i)
-        if (nb + i < N) cp[i] = acc[i];
-    }
-  } else {
-    uint16_t* cp = reinterpret_cast<uint16_t*>(c) + m * ldc + nb;
-    bf16x4 o;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) o[i] = (__bf16)acc[i];
-    if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 7) == 0)) {
-      *reinterpret_cast<bf16x4*>(cp) = o;
-    } else {
-      const u32x2 bits = __builtin_bit_cast(u32x2, o);
-      for (int i = 0; i < 4; ++i)
-        if (nb + i < N) cp[i] = (uint16_t)((i & 1) ? (bits[i >> 1] >> 16) : (bits[i >> 1] & 0xffffu));
-    }
-  }
-}
 
 // ---------------------------------------------------------------------------
 // LDS ring mapping.
@@ -151,10 +78,11 @@ __device__ __forceinline__ u32x4 lds_read16(uint32_t addr) {
   return v;
 }
 
-// Waits for every outstanding LDS read of this wave; the fragments are tied
-// to the wait so no use of them can be scheduled above it.
-template <int NA, int NB>
+// Waits for every outstanding LDS read of this wave; x and y are tied to
+// the wait so no use of them can be scheduled above it.
+template <int pending, int NA, int NB>
 __device__ __forceinline__ void lds_wait(u32x4 (&x)[NA], u32x4 (&y)[NB]) {
+  static_assert(pending == 0, "the reads are consumed right after they land");
 #if defined(__HIP_DEVICE_COMPILE__)
   asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
 #pragma unroll
@@ -232,7 +160,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     const bool live = s < nslices;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      if (wave + 4 * j >= G) break;          // wave-uniform
+      if (G % 4 != 0 && wave + 4 * j >= G) break;  // wave-uniform
       lds_void* dst = (lds_void*)(lds + st * STAGE + (wave + 4 * j) * 512);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsj[j] : rzero, dst, 16,
                                                voff[j] + (uint32_t)(s * BK * 2), 0, 0, 0);
@@ -260,6 +188,10 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     const uint32_t sa = lds_base + (uint32_t)((s % STAGES) * STAGE * 2);
     const uint32_t sw = sa + BM * BK * 2;
     const int ksteps = (int)min<int64_t>(SPS, nsteps - SPS * s);  // fewer only on a ragged final slice
+    // One K step at a time: its fragments are read and waited for in full
+    // before its MFMAs.  (The reads are not prefetched a step ahead: the
+    // compiler does not know these registers fill asynchronously and may copy
+    // them before the wait.)
     for (int ks = 0; ks < ksteps; ++ks) {
       const uint32_t cs = (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16);
       u32x4 fw[NB], fa[MB];
@@ -269,7 +201,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
 #pragma unroll
       for (int j = 0; j < MB; ++j)
         fa[j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
-      lds_wait(fw, fa);
+      lds_wait<0>(fw, fa);
 #pragma unroll
       for (int i = 0; i < NB; ++i)
 #pragma unroll
@@ -373,10 +305,15 @@ hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_
 hipError_t launch_gemm_splitk(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, float* partial,
                               int64_t M, int64_t N, int64_t K, int32_t k_splits, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
-  dim3 grid((unsigned)((N + 16 * kWaves - 1) / (16 * kWaves)), (unsigned)((M + 15) / 16), (unsigned)k_splits);
-  hipLaunchKernelGGL(gemm_kernel, grid, dim3(64 * kWaves), 0, stream, a, lda, w, ldw, (void*)partial, N, 1, M, N,
-                     K / k_splits, M * N);
-  return hipGetLastError();
+  // Split z multiplies the K range [z*kc, (z+1)*kc) with the product kernel
+  // into fp32 partial[z]; the tile configuration is the product's for (M, N).
+  const int64_t kc = K / k_splits;
+  for (int32_t z = 0; z < k_splits; ++z) {
+    const hipError_t e = launch_gemm(a + z * kc, lda, w + z * kc, ldw, partial + (int64_t)z * M * N, N, 1, M, N, kc,
+                                     stream);
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_splitk_reduce(const float* partial, int32_t k_splits, int64_t M, int64_t N, void* c,

@@ -262,16 +262,24 @@ def test_gemm_ragged_k_tails_and_strides(M, K):
     assert np.all(got[:, N:] == 7.0)
 
 
-@pytest.mark.parametrize("M", [1, 16, 17, 33, 65, 129, 300])
-def test_gemm_tile_mappings_agree_bitwise(M):
-    """The LDS-ring mapping (tile shape chosen from M) and the register-direct
-    mapping of the split-K comparator run with one split perform the same
-    per-element instruction sequence, so their fp32 outputs agree bit for bit."""
-    a = synth.normal_bf16_device((M, 2048), 541)
-    w = synth.normal_bf16_device((1000, 2048), 542, std=0.02)
-    ring = bi.bi_gemm(a, w, out_dtype=torch.float32)
-    direct = bi.bi_gemm_splitk(a, w, 1, out_dtype=torch.float32)
-    assert first_mismatch(ring, direct) is None
+@pytest.mark.parametrize("N", [1000, 8192, 20000])
+def test_gemm_tile_configurations_agree_bitwise(N):
+    """The tile configuration follows M and N (every M bracket and N bracket is
+    visited here); each row of c must equal, bit for bit, that row computed
+    alone (M = 1), and agree with the oracle."""
+    K = 2560
+    a = synth.normal_bf16_device((300, K), 541)
+    w = synth.normal_bf16_device((N, K), 542, std=0.02)
+    single = {r: bi.bi_gemm(a[r:r + 1], w, out_dtype=torch.float32) for r in (0, 16, 32, 64, 128, 299)}
+    for M in (16, 17, 33, 65, 129, 257, 300):
+        c = bi.bi_gemm(a[:M], w, out_dtype=torch.float32)
+        for r, ref in single.items():
+            if r < M:
+                assert first_mismatch(c[r:r + 1], ref) is None, (M, r)
+    rows = [0, 299]
+    ah, wh = synth.to_f64(a[rows].cpu()), synth.to_f64(w[:64].cpu())
+    got = torch.cat([single[r][:, :64] for r in rows]).cpu().double().numpy()
+    assert np.all(np.abs(got - oracle.gemm_ref(ah, wh)) <= 1e-3 * oracle.gemm_abs_ref(ah, wh))
 
 
 def test_gemm_lm_head_full_size_sampled():
