@@ -66,6 +66,7 @@ _sig("bi_kv_cache_bytes", c_i32, c_vp, c_i64, ctypes.POINTER(c_sz))
 _sig("bi_slot_mapping", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp)
 _sig("bi_kv_write", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp)
 _sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
+_sig("bi_paged_attention_item_blocks", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
@@ -280,6 +281,12 @@ def workspace_views(cfg: AttnConfig, workspace, num_tokens: int, num_splits: int
     ml = f[:ml_bytes].view(torch.float32).view(R, num_splits, 2)
     acc = f[acc_off: acc_off + R * num_splits * cfg.head_dim * 4].view(torch.float32).view(R, num_splits, cfg.head_dim)
     return ml, acc
+
+
+def bi_paged_attention_item_blocks(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int) -> int:
+    v = c_i32()
+    _check(lib.bi_paged_attention_item_blocks(cfg.handle, num_seqs, num_tokens, max_seq_len, ctypes.byref(v)))
+    return v.value
 
 
 def bi_splitk_attention_heuristic(cfg: AttnConfig, num_seqs, max_seq_len, num_compute_units, waves_per_cu=8):

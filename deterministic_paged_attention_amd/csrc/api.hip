@@ -236,6 +236,26 @@ bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t n
   return ok();
 }
 
+bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                         int32_t max_seq_len, int32_t* blocks) {
+  if (bi_status st = check_cfg(cfg)) return st;
+  if (!blocks || num_seqs < 1 || num_tokens < 0 || max_seq_len < 1)
+    return fail(BI_ERR_INVALID_ARG, "blocks NULL, num_seqs < 1, num_tokens < 0 or max_seq_len < 1");
+  bi::AttnSplitArgs a{};
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = cfg->desc.num_q_heads;
+  a.num_kv_heads = cfg->desc.num_kv_heads;
+  a.log2_group = cfg->log2_group;
+  a.split = cfg->desc.split_size;
+  a.window = cfg->desc.window;
+  a.ns = (int32_t)((max_seq_len + (int64_t)cfg->desc.split_size - 1) / cfg->desc.split_size);
+  const int qb = bi::attn_item_blocks(cfg->desc.head_dim, a);
+  if (qb <= 0) return fail(BI_ERR_HIP, "no usable device to size the launch");
+  *blocks = qb;
+  return ok();
+}
+
 bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                                    int32_t max_seq_len, int32_t num_splits, size_t* bytes) {
   if (bi_status st = check_cfg(cfg)) return st;

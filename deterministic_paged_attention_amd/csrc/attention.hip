@@ -275,7 +275,7 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) 
   __shared__ int carry_sh;
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
-  const int tq = kRowsPerBlock >> a.log2_group;
+  const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;  // query tokens per work item
   if (tid == 0) carry_sh = 0;
   __syncthreads();
   for (int base = 0; base < a.num_seqs; base += 1024) {
@@ -330,7 +330,7 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, int u, int t
   const int q_len = ldc(a.qsl, s + 1) - q0;
   const int k_len = ldc(a.seq_lens, s);
   const SeqSplits sp = seq_splits(q_len, k_len, a.window, a.split);
-  const int tq = kRowsPerBlock >> a.log2_group;
+  const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
   const int sigma = sp.lo + local % sp.n;
   const int rest = local / sp.n;
   it.s = s;
@@ -363,10 +363,10 @@ struct ItemLane {
 };
 
 template <int D>
-__device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const Item& it, int lane) {
+__device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const Item& it, int lane, int blk) {
   constexpr int NSTEP = D / 32;
   const int r = lane & 15, g4 = lane >> 4;
-  const int t = r >> a.log2_group;
+  const int t = blk * (kRowsPerBlock >> a.log2_group) + (r >> a.log2_group);
   const int hh = r & ((1 << a.log2_group) - 1);
   const bool row_ok = it.valid && (t < it.nrow_tok) && (it.q0 + it.tq0 + t < a.num_tokens);
   const int p = it.p_first + t;
@@ -375,7 +375,7 @@ __device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const I
   L.rm.lo = max(a.window > 0 ? max(0, p - a.window + 1) : 0, split_lo);
   L.rm.hi = min(p, split_lo + a.split - 1);
   if (!row_ok || p < 0) { L.rm.lo = 1; L.rm.hi = 0; }
-  // Rows past the block (padding columns of the MFMA) read the block's first
+  // Rows past the item (padding columns of the MFMA) read the item's first
   // row instead: their mask is empty, so their scores never reach any result
   // (each MFMA output column depends only on its own Q column).
   const int tok = min(it.q0 + it.tq0 + (row_ok ? t : 0), max(a.num_tokens - 1, 0));
@@ -388,10 +388,10 @@ __device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const I
 
 template <int D>
 __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item& it, const ItemLane<D>& L,
-                                              const SplitState<D>& st, int lane) {
+                                              const SplitState<D>& st, int lane, int blk) {
   if (L.rm.lo > L.rm.hi) return;
   const int r = lane & 15, g4 = lane >> 4;
-  const int t = r >> a.log2_group;
+  const int t = blk * (kRowsPerBlock >> a.log2_group) + (r >> a.log2_group);
   const int hh = r & ((1 << a.log2_group) - 1);
   const int64_t row = (int64_t)(it.q0 + it.tq0 + t) * a.num_q_heads + (it.kvh << a.log2_group) + hh;
   const int64_t idx = row * a.ns + it.sigma;
@@ -414,15 +414,30 @@ __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item
 // tile k+1 may already belong to the wave's next item (whose description is
 // decoded while the current item is computed).  Which wave
 // computes an item, and when, has no effect on its arithmetic.
+//
+// An item holds QB query-row blocks (QB = 1 for decode-shaped batches, more
+// for prefill-shaped ones, where a loaded K/V tile then serves QB blocks).
+// Every block runs compute_tile exactly as it would alone: the same tile, the
+// same instructions, its own state.  The item's tile range is the union of its
+// blocks' ranges, and a tile outside a row's range leaves that row's state
+// unchanged, so the choice of QB never changes a bit of any row.
 // ---------------------------------------------------------------------------
-template <int D>
+template <int D, int QB>
 struct SplitWave {
   const AttnSplitArgs& a;
   int lane, g4, total, stride, u;
   Item cur, nxt;
-  ItemLane<D> curL;
-  SplitState<D> st;
+  ItemLane<D> curL[QB];
+  SplitState<D> st[QB];
   int ct;  // tile of `cur` being computed
+
+  __device__ __forceinline__ void begin_item() {
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      curL[b] = item_lane<D>(a, cur, lane, b);
+      st[b].init();
+    }
+  }
 
   // Compute tile `ct` of `cur` from Bc while the next tile of the stream loads
   // into Bl.  Returns false once the wave has no item left.
@@ -433,17 +448,18 @@ struct SplitWave {
     const int lend = (in_cur || nxt.valid) ? L.tile_end : lt;  // dead load past the last item
     load_tile(a, L.kvh, L.k_len, lt, lend, tile_pages(L.pt_row, L.last_entry, lt), lane, Bl);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile(st, Bc, curL.q, ct, curL.rm, g4, a.qk_scale_log2);
+#pragma unroll
+    for (int b = 0; b < QB; ++b) compute_tile(st[b], Bc, curL[b].q, ct, curL[b].rm, g4, a.qk_scale_log2);
     __builtin_amdgcn_sched_barrier(0);
     if (in_cur) {
       ++ct;
       return true;
     }
-    write_partial(a, cur, curL, st, lane);
-    st.init();
+#pragma unroll
+    for (int b = 0; b < QB; ++b) write_partial(a, cur, curL[b], st[b], lane, b);
     if (!nxt.valid) return false;
     cur = nxt;
-    curL = item_lane<D>(a, cur, lane);  // Q loads overlap the tile loads already in flight
+    begin_item();  // Q loads overlap the tile loads already in flight
     u += stride;
     ct = cur.tile_begin;
     nxt = decode_item(a, u + stride, total);
@@ -451,13 +467,13 @@ struct SplitWave {
   }
 };
 
-template <int D>
+template <int D, int QB>
 __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const AttnSplitArgs a) {
   const int lane = threadIdx.x & 63;
   // Wave index, made visibly wave-uniform so everything derived from the
   // item index stays in scalar registers (scalar page-table loads).
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  SplitWave<D> w{a};
+  SplitWave<D, QB> w{a};
   w.lane = lane;
   w.g4 = lane >> 4;
   w.total = ldc(a.plan, a.num_seqs);
@@ -465,9 +481,8 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
   w.u = blockIdx.x * kSplitWaves + wave;
   w.cur = decode_item(a, w.u, w.total);
   if (!w.cur.valid) return;
-  w.curL = item_lane<D>(a, w.cur, lane);
+  w.begin_item();
   w.nxt = decode_item(a, w.u + w.stride, w.total);
-  w.st.init();
   w.ct = w.cur.tile_begin;
   TileData<D> buf0, buf1;
   load_tile(a, w.cur.kvh, w.cur.k_len, w.ct, w.cur.tile_end, tile_pages(w.cur.pt_row, w.cur.last_entry, w.ct),
@@ -528,8 +543,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
 }
 
 // Workgroups of the persistent split kernel that the current device keeps
-// resident at once (computed once per device and head size).
-template <int D>
+// resident at once (computed once per device, head size and item width).
+template <int D, int QB>
 int resident_split_groups() {
   static int cached[64] = {0};
   int dev = 0;
@@ -537,22 +552,53 @@ int resident_split_groups() {
   if (cached[dev] > 0) return cached[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<D>, 64 * kSplitWaves, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_kernel<D, QB>, 64 * kSplitWaves, 0) !=
       hipSuccess)
     return 0;
   cached[dev] = max(1, cus * max(per_cu, 1));
   return cached[dev];
 }
 
-template <int D>
-hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
-  const int groups = resident_split_groups<D>();
+template <int D, int QB>
+hipError_t split_launch_qb(AttnSplitArgs a, hipStream_t stream) {
+  a.qblocks = QB;
+  const int groups = resident_split_groups<D, QB>();
   if (groups <= 0) return hipErrorInvalidDevice;
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_split_kernel<D>, dim3(groups), dim3(64 * kSplitWaves), 0, stream, a);
+  hipLaunchKernelGGL((attn_split_kernel<D, QB>), dim3(groups), dim3(64 * kSplitWaves), 0, stream, a);
   return hipGetLastError();
+}
+
+// Item width: wide items (kWideBlocks query blocks) when the batch is
+// prefill-shaped — on average at least that many blocks per sequence — and
+// still yields at least one wide item per resident wave (estimated with every
+// row meeting all ns splits); one block otherwise.  Only the work mapping
+// depends on this choice, never the arithmetic of a row.  At head_dim 256 the
+// state of a second block does not fit the register file, so items stay one
+// block wide.
+constexpr int kWideBlocks = 4;
+
+template <int D>
+int item_blocks(const AttnSplitArgs& a) {
+  if constexpr (D <= 128) {
+    const int64_t tq = kRowsPerBlock >> a.log2_group;
+    const int64_t wide_items = ((int64_t)a.num_tokens + kWideBlocks * tq - 1) / (kWideBlocks * tq) *
+                               a.num_kv_heads * a.ns;
+    const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
+    if ((int64_t)a.num_tokens >= kWideBlocks * tq * (int64_t)a.num_seqs && wide_items >= wide_waves)
+      return kWideBlocks;
+  }
+  return 1;
+}
+
+template <int D>
+hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
+  if constexpr (D <= 128) {
+    if (item_blocks<D>(a) == kWideBlocks) return split_launch_qb<D, kWideBlocks>(a, stream);
+  }
+  return split_launch_qb<D, 1>(a, stream);
 }
 
 template <int D>
@@ -571,6 +617,15 @@ hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t s
     case 128: return split_launch<128>(a, stream);
     case 256: return split_launch<256>(a, stream);
     default: return hipErrorInvalidValue;
+  }
+}
+
+int attn_item_blocks(int head_dim, const AttnSplitArgs& a) {
+  switch (head_dim) {
+    case 64: return item_blocks<64>(a);
+    case 128: return item_blocks<128>(a);
+    case 256: return item_blocks<256>(a);
+    default: return 0;
   }
 }
 

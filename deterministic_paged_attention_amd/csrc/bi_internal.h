@@ -36,6 +36,7 @@ struct AttnSplitArgs {
   float2* ws_ml;             // [R][ns]
   float* ws_acc;             // [R][ns][D]
   int32_t* plan;             // [num_seqs + 1]: first work item of each sequence, total last
+  int32_t qblocks;           // query-row blocks per work item (set by the launcher)
 };
 
 struct AttnMergeArgs {
@@ -53,6 +54,9 @@ struct AttnMergeArgs {
 };
 
 hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t stream);
+// Query-row blocks per work item the split launch would use for these arguments
+// (needs the current device; 0 on failure).
+int attn_item_blocks(int head_dim, const AttnSplitArgs& a);
 hipError_t launch_attn_merge(int head_dim, const AttnMergeArgs& a, hipStream_t stream);
 
 hipError_t launch_slot_mapping(const int32_t* page_table, int32_t stride, const int32_t* seq_lens,

@@ -165,6 +165,18 @@ bi_status bi_paged_attention(const bi_attn_config* cfg,
                              void* workspace_dev, size_t workspace_bytes,
                              void* out_dev, void* stream);
 
+/* Work mapping of the split phase (diagnostic).  A work item is one
+ * (sequence, group of query-row blocks, KV head, split); *blocks receives the
+ * number of 16-column query-row blocks per item the split phase would use for
+ * a batch of this shape: 1 for decode-shaped batches, 4 for prefill-shaped ones
+ * at head_dim <= 128, so that one loaded K/V tile serves four blocks.  Either
+ * mapping performs the same arithmetic for every row (each block runs the same
+ * per-tile computation on its own state; tiles outside a row's key range leave
+ * it unchanged), so the value affects speed only.  Needs a current device
+ * (BI_ERR_HIP without one). */
+bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                         int32_t max_seq_len, int32_t* blocks);
+
 /* The two phases of bi_paged_attention, separately: the split phase writes the
  * workspace partials described above; the merge phase reads them and writes
  * the output.  bi_paged_attention == split then merge on the same stream. */

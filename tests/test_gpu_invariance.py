@@ -123,6 +123,11 @@ def test_prefill_chunks_and_token_by_token_agree(geom, window):
     cfg = bi.AttnConfig(geom.num_q_heads, geom.num_kv_heads, geom.head_dim, split_size=256, window=window)
     lens = [700, 1300] if window == 0 else [1300, 600]
     reqs = {i: Request(500 + i + window, L, geom) for i, L in enumerate(lens)}
+    if geom is LLAMA:
+        # the one-shot prefill runs wide work items, token by token runs one-block items:
+        # the comparison below is then also a cross-mapping check
+        assert bi.bi_paged_attention_item_blocks(cfg, 2, sum(lens), max(lens)) == 4
+        assert bi.bi_paged_attention_item_blocks(cfg, 2, 2, max(lens)) == 1
     one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=3)
     assert len(one_shot) == sum(lens)
     for budget, offset, pseed in [(16, 0, 4), (128, 37, 5), (512, 5, 6), (1, 0, 7)]:
