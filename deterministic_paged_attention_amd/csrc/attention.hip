@@ -118,6 +118,15 @@ struct RowMask {
   int lo, hi;
 };
 
+// Per-lane part of an item's query-row block: this lane's row, its visible
+// keys inside the split, and its Q fragment (B operand of S^T = K Q^T: step
+// st, lane group g4 holds head-dim chunk 4*st + g4).
+template <int D>
+struct ItemLane {
+  RowMask rm;
+  bf16x8 q[D / 32];
+};
+
 // Page-table entries of the two 16-key halves of a tile.  The read is
 // unconditional (its index is clamped to the last entry the sequence uses, so
 // entries past ceil(k_len / 16) are never read) and its result is first needed
@@ -183,52 +192,73 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
   }
 }
 
-// One online-softmax step over a 32-key tile for this lane's row.  A row with
-// no visible key in the tile keeps (m, l, acc) bit-for-bit (select, not update).
-template <int D>
-__device__ __forceinline__ void compute_tile(SplitState<D>& st, const TileData<D>& t, const bf16x8* qf, int tile,
-                                             const RowMask& rm, int g4, float qk_scale_log2) {
+// One online-softmax step over a 32-key tile for the rows of QB query-row
+// blocks (this lane's row of each).  Each phase runs over the blocks before the
+// next phase starts, so the blocks' independent MFMA chains and reductions can
+// overlap; every row still goes through exactly the operations, in exactly the
+// order, it would alone.  A row with no visible key in the tile keeps
+// (m, l, acc) bit-for-bit (select, not update).
+template <int D, int QB>
+__device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const TileData<D>& t,
+                                             const ItemLane<D> (&L)[QB], int tile, int g4, float qk_scale_log2) {
   constexpr int NSTEP = D / 32;
   constexpr int NBLK = D / 16;
   const int kb = tile << 5;
-  // Scores: lane holds keys kb + 16b + 4*g4 + i (i = 0..3) of its row.
-  float x[2][4];
+  // Scores: lane holds keys kb + 16h + 4*g4 + i (i = 0..3) of its row.
+  float x[QB][2][4];
 #pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    f32x4 sc = {0.f, 0.f, 0.f, 0.f};
+  for (int h = 0; h < 2; ++h) {
+    f32x4 sc[QB];
 #pragma unroll
-    for (int s = 0; s < NSTEP; ++s) sc = mfma16x16x32(__builtin_bit_cast(bf16x8, t.kf[b][s]), qf[s], sc);
+    for (int b = 0; b < QB; ++b) sc[b] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const int key = kb + 16 * b + 4 * g4 + i;
-      const bool ok = key >= rm.lo && key <= rm.hi;
-      x[b][i] = ok ? sc[i] * qk_scale_log2 : -INFINITY;
-    }
+    for (int s = 0; s < NSTEP; ++s)
+#pragma unroll
+      for (int b = 0; b < QB; ++b) sc[b] = mfma16x16x32(__builtin_bit_cast(bf16x8, t.kf[h][s]), L[b].q[s], sc[b]);
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int key = kb + 16 * h + 4 * g4 + i;
+        const bool ok = key >= L[b].rm.lo && key <= L[b].rm.hi;
+        x[b][h][i] = ok ? sc[b][i] * qk_scale_log2 : -INFINITY;
+      }
   }
-  float tmax = x[0][0];
+  float tmax[QB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < QB; ++b) {
+    tmax[b] = x[b][0][0];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) tmax = fmaxf(tmax, x[b][i]);
-  tmax = row4_max(tmax);
-  const bool live = tmax != -INFINITY;  // this row sees at least one key here
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) tmax[b] = fmaxf(tmax[b], x[b][h][i]);
+  }
+#pragma unroll
+  for (int b = 0; b < QB; ++b) tmax[b] = row4_max(tmax[b]);
 
-  const float m_new = fmaxf(st.m, tmax);
-  const float alpha = (st.m == -INFINITY) ? 0.f : exp2_hw(st.m - m_new);
-  __bf16 pb[2][4];
-  float rs = 0.f;
+  bool live[QB];
+  float m_new[QB], alpha[QB], rs[QB];
+  bf16x8 pfrag[QB];
 #pragma unroll
-  for (int b = 0; b < 2; ++b)
+  for (int b = 0; b < QB; ++b) {
+    live[b] = tmax[b] != -INFINITY;  // this row sees at least one key here
+    m_new[b] = fmaxf(st[b].m, tmax[b]);
+    alpha[b] = (st[b].m == -INFINITY) ? 0.f : exp2_hw(st[b].m - m_new[b]);
+    __bf16 pb[2][4];
+    rs[b] = 0.f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const float e = (x[b][i] != -INFINITY) ? exp2_hw(x[b][i] - m_new) : 0.f;
-      pb[b][i] = (__bf16)e;
-      rs += (float)pb[b][i];
-    }
-  rs = row4_sum(rs);
-  const float l_new = __builtin_fmaf(alpha, st.l, rs);
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const float e = (x[b][h][i] != -INFINITY) ? exp2_hw(x[b][h][i] - m_new[b]) : 0.f;
+        pb[h][i] = (__bf16)e;
+        rs[b] += (float)pb[h][i];
+      }
+    pfrag[b] = bf16x8{pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
+  }
+#pragma unroll
+  for (int b = 0; b < QB; ++b) rs[b] = row4_sum(rs[b]);
 
-  const bf16x8 pfrag = {pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
 #pragma unroll
   for (int n = 0; n < NBLK; ++n) {
     // De-interleave head-dim block n (e = n & 1) from the loaded pairs:
@@ -239,12 +269,19 @@ __device__ __forceinline__ void compute_tile(SplitState<D>& st, const TileData<D
                       __builtin_amdgcn_perm(w0.w, w0.z, sel) & t.vmask[0].y,
                       __builtin_amdgcn_perm(w1.y, w1.x, sel) & t.vmask[1].x,
                       __builtin_amdgcn_perm(w1.w, w1.z, sel) & t.vmask[1].y};
-    const f32x4 cin = st.acc[n] * alpha;
-    const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag, cin);
-    st.acc[n] = live ? res : st.acc[n];
+#pragma unroll
+    for (int b = 0; b < QB; ++b) {
+      const f32x4 cin = st[b].acc[n] * alpha[b];
+      const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag[b], cin);
+      st[b].acc[n] = live[b] ? res : st[b].acc[n];
+    }
   }
-  st.m = live ? m_new : st.m;
-  st.l = live ? l_new : st.l;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) {
+    const float l_new = __builtin_fmaf(alpha[b], st[b].l, rs[b]);
+    st[b].m = live[b] ? m_new[b] : st[b].m;
+    st[b].l = live[b] ? l_new : st[b].l;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -352,16 +389,8 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, int u, int t
   return it;
 }
 
-// Per-lane part of an item: this lane's query row (token t of the block, head
-// hh of the GQA group), its visible keys inside the split, and its Q fragment
-// (B operand of S^T = K Q^T: step st, lane group g4 holds head-dim chunk
-// 4*st + g4).
-template <int D>
-struct ItemLane {
-  RowMask rm;
-  bf16x8 q[D / 32];
-};
-
+// This lane's query row in block blk of an item (token t of the item, head hh
+// of the GQA group).
 template <int D>
 __device__ __forceinline__ ItemLane<D> item_lane(const AttnSplitArgs& a, const Item& it, int lane, int blk) {
   constexpr int NSTEP = D / 32;
@@ -448,8 +477,7 @@ struct SplitWave {
     const int lend = (in_cur || nxt.valid) ? L.tile_end : lt;  // dead load past the last item
     load_tile(a, L.kvh, L.k_len, lt, lend, tile_pages(L.pt_row, L.last_entry, lt), lane, Bl);
     __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int b = 0; b < QB; ++b) compute_tile(st[b], Bc, curL[b].q, ct, curL[b].rm, g4, a.qk_scale_log2);
+    compute_tile<D, QB>(st, Bc, curL, ct, g4, a.qk_scale_log2);
     __builtin_amdgcn_sched_barrier(0);
     if (in_cur) {
       ++ct;
