@@ -75,6 +75,15 @@ _sig("bi_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c
 _sig("bi_gemm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_check_page_table", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_check_write_plan", c_i32, c_vp, c_i32, c_vp, c_i32, c_i32)
+_sig("bi_argmax", c_i32, c_vp, c_i64, c_i64, c_i64, c_vp, c_vp)
+_sig("bi_prefix_cache_create", c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_vp))
+_sig("bi_prefix_cache_destroy", None, c_vp)
+_sig("bi_prefix_cache_match", c_i32, c_vp, c_vp, c_i64, c_vp, c_i32, P_i32)
+_sig("bi_prefix_cache_alloc", c_i32, c_vp, c_i32, c_vp)
+_sig("bi_prefix_cache_register", c_i32, c_vp, c_i32, c_i32, c_i32, c_vp, P_i32)
+_sig("bi_prefix_cache_release", c_i32, c_vp, c_vp, c_i32)
+_sig("bi_prefix_cache_writable", c_i32, c_vp, c_vp, c_i32)
+_sig("bi_prefix_cache_stats", c_i32, c_vp, c_vp)
 _sig("bi_splitk_attention_heuristic", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, P_i32)
 _sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_splitk", c_i32, *_ATTN_ARGS, c_i32, c_vp, c_sz, c_vp, c_vp)
@@ -434,6 +443,77 @@ def bi_check_write_plan(slot_mapping, page_writable, num_pages, page_size):
     pw = None if page_writable is None else np.ascontiguousarray(np.asarray(page_writable, dtype=np.uint8))
     _check(lib.bi_check_write_plan(sm.ctypes.data if sm.size else None, sm.shape[0],
                                    None if pw is None else pw.ctypes.data, num_pages, page_size))
+
+
+def bi_argmax(x, out=None, stream=None):
+    """Greedy sampling over fp32 rows: smallest index of the row maximum."""
+    torch = _torch()
+    _need(x, torch.float32, "x")
+    R, n = x.shape
+    if out is None:
+        out = torch.empty((R,), dtype=torch.int32, device=x.device)
+    if x.stride(1) != 1:
+        raise ValueError("rows of x must be contiguous")
+    _check(lib.bi_argmax(_ptr(x), x.stride(0) if R > 1 else n, R, n, _ptr(out), _stream(stream)))
+    return out
+
+
+class PrefixCache:
+    """Host-side prefix cache of KV pages (the C ABI's bi_prefix_cache_*);
+    arguments and results are Python lists of ints."""
+
+    def __init__(self, num_pages: int, page_size: int = 16, hash_bits: int = 64):
+        h = c_vp()
+        _check(lib.bi_prefix_cache_create(num_pages, page_size, hash_bits, ctypes.byref(h)))
+        self.handle = h
+        self.num_pages = num_pages
+        self.page_size = page_size
+
+    def __del__(self):
+        if getattr(self, "handle", None) and lib is not None:
+            lib.bi_prefix_cache_destroy(self.handle)
+            self.handle = None
+
+    @staticmethod
+    def _arr(values, dtype=np.int32):
+        return np.ascontiguousarray(np.asarray(values, dtype=dtype))
+
+    def match(self, tokens, max_pages: int):
+        t = self._arr(tokens)
+        out = np.zeros(max(max_pages, 1), dtype=np.int32)
+        k = c_i32()
+        _check(lib.bi_prefix_cache_match(self.handle, t.ctypes.data if t.size else None, t.size, out.ctypes.data,
+                                         max_pages, ctypes.byref(k)))
+        return out[:k.value].tolist()
+
+    def alloc(self, n: int):
+        out = np.zeros(max(n, 1), dtype=np.int32)
+        _check(lib.bi_prefix_cache_alloc(self.handle, n, out.ctypes.data))
+        return out[:n].tolist()
+
+    def register(self, page: int, parent: int, depth: int, tokens):
+        """Returns the id of an identical cached page (page stays private), or -1."""
+        t = self._arr(tokens)
+        if t.size != self.page_size:
+            raise ValueError("a page holds exactly page_size tokens")
+        ex = c_i32()
+        _check(lib.bi_prefix_cache_register(self.handle, page, parent, depth, t.ctypes.data, ctypes.byref(ex)))
+        return ex.value
+
+    def release(self, pages):
+        p = self._arr(pages)
+        _check(lib.bi_prefix_cache_release(self.handle, p.ctypes.data if p.size else None, p.size))
+
+    def writable(self):
+        m = np.zeros(self.num_pages, dtype=np.uint8)
+        _check(lib.bi_prefix_cache_writable(self.handle, m.ctypes.data, self.num_pages))
+        return m
+
+    def stats(self):
+        """(free pages, registered pages, evictable pages, evictions so far)"""
+        s = np.zeros(4, dtype=np.int64)
+        _check(lib.bi_prefix_cache_stats(self.handle, s.ctypes.data))
+        return tuple(int(v) for v in s)
 
 
 def bi_version() -> int:

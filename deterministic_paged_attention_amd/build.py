@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip", "glue.hip"]
+SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip", "glue.hip", "prefix_cache.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 ARCH = "gfx950"
@@ -33,12 +33,19 @@ FLAGS = [
 ]
 
 
+CXX = os.environ.get("CXX", "g++")
+CXX_FLAGS = ["-O2", "-fPIC", "-std=c++17", "-Wall"]   # host-only sources (.cpp)
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, os.path.splitext(src)[0] + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    if src.endswith(".cpp"):
+        cmd = [CXX, *CXX_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
+    else:
+        cmd = [HIPCC, *FLAGS, "-c", os.path.join(CSRC, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
-        raise RuntimeError(f"hipcc failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        raise RuntimeError(f"compile failed for {src}:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     return obj
 
 

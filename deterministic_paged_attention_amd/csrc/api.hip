@@ -5,6 +5,7 @@
 
 #include "../../include/bi.h"
 #include "bi_internal.h"
+#include "prefix_cache.h"
 
 #include <cmath>
 #include <cstdarg>
@@ -574,6 +575,81 @@ bi_status bi_check_page_table(const int32_t* page_table_host, int32_t page_table
         return fail(BI_ERR_OUT_OF_RANGE, "sequence %d: q_len %d outside [1, k_len = %d]", s, q_len, k_len);
     }
   }
+  return ok();
+}
+
+bi_status bi_argmax(const float* x_dev, int64_t ld, int64_t rows, int64_t n, int32_t* out_dev, void* stream) {
+  if (rows < 0 || n < 1 || ld < n) return fail(BI_ERR_INVALID_ARG, "rows >= 0, n >= 1 and ld >= n required");
+  if (rows > 0x7fffffffLL) return fail(BI_ERR_OUT_OF_RANGE, "too many rows");
+  if (rows == 0) return ok();
+  if (!x_dev || !out_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  return hip_status(bi::launch_argmax(x_dev, ld, rows, n, out_dev, (hipStream_t)stream), "argmax launch");
+}
+
+}  // extern "C"
+
+struct bi_prefix_cache {
+  bi::PrefixCache impl;
+  bi_prefix_cache(int32_t n, int32_t p, int32_t bits) : impl(n, p, bits) {}
+};
+
+extern "C" {
+
+bi_status bi_prefix_cache_create(int32_t num_pages, int32_t page_size, int32_t hash_bits, bi_prefix_cache** out) {
+  if (!out || num_pages < 1 || page_size < 1 || hash_bits < 0 || hash_bits > 64)
+    return fail(BI_ERR_INVALID_ARG, "num_pages >= 1, page_size >= 1, hash_bits in [0, 64] and out required");
+  *out = nullptr;
+  bi_prefix_cache* c = new (std::nothrow) bi_prefix_cache(num_pages, page_size, hash_bits);
+  if (!c) return fail(BI_ERR_OUT_OF_RANGE, "out of host memory");
+  *out = c;
+  return ok();
+}
+
+void bi_prefix_cache_destroy(bi_prefix_cache* cache) { delete cache; }
+
+bi_status bi_prefix_cache_match(bi_prefix_cache* cache, const int32_t* tokens, int64_t num_tokens,
+                                int32_t* pages_out, int32_t max_pages, int32_t* num_matched) {
+  if (!cache || !num_matched || num_tokens < 0 || max_pages < 0 || (num_tokens > 0 && !tokens) ||
+      (max_pages > 0 && !pages_out))
+    return fail(BI_ERR_INVALID_ARG, "bad arguments to bi_prefix_cache_match");
+  *num_matched = cache->impl.match(tokens, num_tokens, pages_out, max_pages);
+  return ok();
+}
+
+bi_status bi_prefix_cache_alloc(bi_prefix_cache* cache, int32_t n, int32_t* pages_out) {
+  if (!cache || n < 0 || (n > 0 && !pages_out)) return fail(BI_ERR_INVALID_ARG, "bad arguments to bi_prefix_cache_alloc");
+  if (!cache->impl.alloc(n, pages_out))
+    return fail(BI_ERR_OUT_OF_RANGE, "cannot provide %d pages (all others referenced)", n);
+  return ok();
+}
+
+bi_status bi_prefix_cache_register(bi_prefix_cache* cache, int32_t page, int32_t parent, int32_t depth,
+                                   const int32_t* tokens, int32_t* existing) {
+  if (!cache || !tokens || !existing || page < 0 || page >= cache->impl.num_pages() || parent < -1 ||
+      parent >= cache->impl.num_pages())
+    return fail(BI_ERR_INVALID_ARG, "bad arguments to bi_prefix_cache_register");
+  const int r = cache->impl.register_page(page, parent, depth, tokens, existing);
+  if (r == -1) return fail(BI_ERR_WRITE_CONFLICT, "page %d is shared or already registered", page);
+  if (r == -2) return fail(BI_ERR_INVALID_ARG, "page %d: parent %d / depth %d inconsistent", page, parent, depth);
+  return ok();
+}
+
+bi_status bi_prefix_cache_release(bi_prefix_cache* cache, const int32_t* pages, int32_t n) {
+  if (!cache || n < 0 || (n > 0 && !pages)) return fail(BI_ERR_INVALID_ARG, "bad arguments to bi_prefix_cache_release");
+  if (!cache->impl.release(pages, n)) return fail(BI_ERR_INVALID_ARG, "a page would lose a reference it does not hold");
+  return ok();
+}
+
+bi_status bi_prefix_cache_writable(const bi_prefix_cache* cache, uint8_t* mask_out, int32_t num_pages) {
+  if (!cache || !mask_out || num_pages != cache->impl.num_pages())
+    return fail(BI_ERR_INVALID_ARG, "mask must cover exactly the cache's pages");
+  for (int32_t p = 0; p < num_pages; ++p) mask_out[p] = cache->impl.writable(p) ? 1 : 0;
+  return ok();
+}
+
+bi_status bi_prefix_cache_stats(const bi_prefix_cache* cache, int64_t* stats_out) {
+  if (!cache || !stats_out) return fail(BI_ERR_INVALID_ARG, "bad arguments to bi_prefix_cache_stats");
+  cache->impl.stats(stats_out);
   return ok();
 }
 

@@ -1,5 +1,6 @@
 // Per-row and elementwise glue of a decoder step: embedding gather, per-head
-// q/k RMSNorm fused with rotary position embedding, residual add, gated GELU.
+// q/k RMSNorm fused with rotary position embedding, residual add, gated GELU,
+// and greedy sampling (argmax over a logits row).
 //
 // The pages define the step only as the cold causal forward Forward(W, h)
 // (Vosti deep-dive blog (深入解析 Vosti), §2, Theorem 4.1); the layer details
@@ -120,6 +121,52 @@ __global__ __launch_bounds__(256) void gated_gelu_kernel(const uint16_t* in, int
   out[r * ld_out + i] = f32_to_bf16(gl * u);
 }
 
+// Greedy sampling: out[row] = the smallest index i with x[row, i] maximal
+// (NaN never wins; an all-NaN row gives 0).  One workgroup per row; each
+// thread scans a strided slice in increasing index, then (value, index) pairs
+// are combined by "larger value, else smaller index" — a total order, so the
+// result is the same whatever the combining tree.
+struct ArgBest {
+  float v;
+  int64_t i;  // -1: nothing seen
+};
+
+__device__ __forceinline__ ArgBest arg_better(ArgBest a, ArgBest b) {
+  if (a.i < 0) return b;
+  if (b.i < 0) return a;
+  if (a.v > b.v || (a.v == b.v && a.i < b.i)) return a;
+  return b;
+}
+
+__global__ __launch_bounds__(256) void argmax_kernel(const float* x, int64_t ld, int64_t n, int32_t* out) {
+  __shared__ float sv[4];
+  __shared__ int64_t si[4];
+  const float* xr = x + (int64_t)blockIdx.x * ld;
+  ArgBest b{0.f, -1};
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    const float v = xr[i];
+    if (v == v && (b.i < 0 || v > b.v)) b = ArgBest{v, i};
+  }
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    ArgBest o;
+    o.v = __shfl_xor(b.v, off);
+    o.i = __shfl_xor(b.i, off);
+    b = arg_better(b, o);
+  }
+  const int wave = threadIdx.x >> 6;
+  if ((threadIdx.x & 63) == 0) {
+    sv[wave] = b.v;
+    si[wave] = b.i;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    ArgBest r{sv[0], si[0]};
+    for (int w = 1; w < 4; ++w) r = arg_better(r, ArgBest{sv[w], si[w]});
+    out[blockIdx.x] = r.i < 0 ? 0 : (int32_t)r.i;
+  }
+}
+
 unsigned blocks_for(int64_t n) { return (unsigned)((n + 255) / 256); }
 
 }  // namespace
@@ -149,6 +196,12 @@ hipError_t launch_add(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t
                       int64_t rows, int64_t n, hipStream_t stream) {
   if (rows * n == 0) return hipSuccess;
   hipLaunchKernelGGL(add_kernel, dim3(blocks_for(rows * n)), dim3(256), 0, stream, a, lda, b, ldb, c, ldc, rows, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_argmax(const float* x, int64_t ld, int64_t rows, int64_t n, int32_t* out, hipStream_t stream) {
+  if (rows == 0) return hipSuccess;
+  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x, ld, n, out);
   return hipGetLastError();
 }
 

@@ -282,6 +282,65 @@ bi_status bi_check_write_plan(const int32_t* slot_mapping_host, int32_t num_toke
                               int32_t page_size);
 
 /* ------------------------------------------------------------------------ */
+/* Greedy sampling: out[t] = the smallest index i with x[t, i] maximal over  */
+/* the row (NaN entries never win; a row of NaN gives 0).  x fp32 [rows][n]  */
+/* with row stride ld; out int32 [rows].  Deterministic for any row count.   */
+/* ------------------------------------------------------------------------ */
+bi_status bi_argmax(const float* x_dev, int64_t ld, int64_t rows, int64_t n, int32_t* out_dev, void* stream);
+
+/* ------------------------------------------------------------------------ */
+/* Prefix cache of KV pages (host side; Vosti deep-dive blog, §3.2           */
+/* engineering constraints "exact prefix matching" and "separate cache reuse */
+/* from generation", §5.4).  Tracks which physical page holds the KV of      */
+/* which token prefix.  A rolling hash over the prefix only nominates        */
+/* candidates; a page is reused only if its tokens, its depth and its parent */
+/* page match exactly.  Registered pages are immutable and shared; new KV    */
+/* goes to private pages, registered once the step that fills them is done.  */
+/* Under memory pressure only unreferenced leaves are evicted (least         */
+/* recently used first), so a parent cannot be recycled while a retained    */
+/* child names it.  All arrays are host arrays.  Not thread-safe.            */
+/* ------------------------------------------------------------------------ */
+typedef struct bi_prefix_cache bi_prefix_cache; /* opaque */
+
+/* hash_bits in [0, 64]: bits of the rolling hash kept (fewer force
+ * collisions, for testing; 64 in normal use). */
+bi_status bi_prefix_cache_create(int32_t num_pages, int32_t page_size, int32_t hash_bits, bi_prefix_cache** out);
+void      bi_prefix_cache_destroy(bi_prefix_cache* cache);
+
+/* Longest run of cached pages holding tokens[0 : page_size*k) exactly, k <=
+ * max_pages; pages_out[0..k) receive them, each acquired (one reference).
+ * A caller that must still compute the last prompt position passes
+ * max_pages = (num_tokens - 1) / page_size. */
+bi_status bi_prefix_cache_match(bi_prefix_cache* cache, const int32_t* tokens, int64_t num_tokens,
+                                int32_t* pages_out, int32_t max_pages, int32_t* num_matched);
+
+/* n private pages (one reference each, writable), from free pages first,
+ * then by evicting unreferenced leaves.  All or nothing: BI_ERR_OUT_OF_RANGE
+ * and no change if n pages cannot be provided. */
+bi_status bi_prefix_cache_alloc(bi_prefix_cache* cache, int32_t n, int32_t* pages_out);
+
+/* Registers private page `page` (held by exactly one reference) as the
+ * cached page of tokens[0 : page_size) at `depth` below `parent` (-1 at
+ * depth 0; a parent must be registered, at depth - 1).  Call only after the
+ * writes that fill the page have completed.  If an identical entry already
+ * exists, *existing receives its page id and `page` stays private
+ * (*existing = -1 otherwise).  BI_ERR_WRITE_CONFLICT if `page` is shared or
+ * already registered, BI_ERR_INVALID_ARG on a bad parent or depth. */
+bi_status bi_prefix_cache_register(bi_prefix_cache* cache, int32_t page, int32_t parent, int32_t depth,
+                                   const int32_t* tokens, int32_t* existing);
+
+/* Drops one reference from each listed page (negative ids are skipped).
+ * BI_ERR_INVALID_ARG, with no change, if a page would drop below zero. */
+bi_status bi_prefix_cache_release(bi_prefix_cache* cache, const int32_t* pages, int32_t n);
+
+/* mask_out[p] = 1 iff page p may be written (private and unregistered):
+ * the page_writable argument of bi_check_write_plan. */
+bi_status bi_prefix_cache_writable(const bi_prefix_cache* cache, uint8_t* mask_out, int32_t num_pages);
+
+/* stats_out[0..4) = free pages, registered pages, evictable pages, evictions. */
+bi_status bi_prefix_cache_stats(const bi_prefix_cache* cache, int64_t* stats_out);
+
+/* ------------------------------------------------------------------------ */
 /* Non-invariant comparators, for measurement only (never used by the        */
 /* invariant path).  The pages name split-K, whose reduction tree follows    */
 /* the shape, as what batch invariance gives up (LLM-42 summary, §1-§2).     */

@@ -20,11 +20,13 @@ from .attention import (attention_ref, attention_probs_ref, split_partials_ref, 
                         dense_attention_bruteforce, LOG2E)
 from .rmsnorm import rmsnorm_ref
 from .gemm import gemm_ref, gemm_abs_ref
-from .decoder import embedding_ref, rope_ref, qk_norm_rope_ref, add_ref, gated_gelu_ref, gelu_tanh
+from .decoder import embedding_ref, rope_ref, qk_norm_rope_ref, add_ref, gated_gelu_ref, gelu_tanh, argmax_ref
+from .prefix_cache import PrefixCacheRef
 
 __all__ = [
     "slot_mapping_ref", "kv_write_ref", "gather_prefix", "row_positions",
     "attention_ref", "attention_probs_ref", "split_partials_ref", "merge_ref",
     "dense_attention_bruteforce", "LOG2E", "rmsnorm_ref", "gemm_ref", "gemm_abs_ref",
     "embedding_ref", "rope_ref", "qk_norm_rope_ref", "add_ref", "gated_gelu_ref", "gelu_tanh",
+    "PrefixCacheRef", "argmax_ref",
 ]

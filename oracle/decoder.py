@@ -66,3 +66,17 @@ def gated_gelu_ref(x):
     x = np.asarray(x, dtype=np.float64)
     F = x.shape[1] // 2
     return gelu_tanh(x[:, :F]) * x[:, F:]
+
+
+def argmax_ref(x):
+    """Greedy sampling over rows of x [R, n]: the smallest index of a row's
+    maximum, ignoring NaN entries; 0 for a row that is all NaN."""
+    x = np.asarray(x, dtype=np.float64)
+    out = np.zeros(x.shape[0], dtype=np.int64)
+    for r in range(x.shape[0]):
+        best = None
+        for i, v in enumerate(x[r]):
+            if v == v and (best is None or v > x[r, best]):
+                best = i
+        out[r] = 0 if best is None else best
+    return out

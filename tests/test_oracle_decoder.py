@@ -64,3 +64,13 @@ def test_gated_gelu_and_add_and_embedding():
     e = oracle.embedding_ref(table, [3, 0, 6, 9, -1])
     np.testing.assert_array_equal(e[:3], table[[3, 0, 6]])
     assert (e[3:] == 0).all()
+
+
+def test_argmax_ref_ties_nan_and_infinities():
+    x = np.array([[1.0, 3.0, 3.0, -1.0],          # tie: first index
+                  [np.nan, -np.inf, -np.inf, np.nan],   # NaN never wins; tie of -inf: first
+                  [np.nan, np.nan, np.nan, np.nan],     # all NaN: 0
+                  [-5.0, np.inf, 2.0, np.inf]])
+    assert oracle.argmax_ref(x).tolist() == [1, 1, 0, 1]
+    r = np.random.default_rng(7).standard_normal((5, 100))
+    assert oracle.argmax_ref(r).tolist() == np.argmax(r, axis=1).tolist()
