@@ -22,6 +22,9 @@ Other workloads (one JSON line each, same keys; not the headline):
                             requests), chunk budgets {16, 128, 512} and token by token
   --workload gemma          one decode step of a 34-layer Gemma-3-4B-shaped decoder
                             (replayed as one HIP graph)
+  --workload agentic        4 sessions x 6 turns through the engine on that decoder:
+                            16K-token prompts over an 8K cached shared prefix, +256
+                            input and 768 output tokens per turn, 0.5 s user delay
 """
 from __future__ import annotations
 
@@ -679,12 +682,116 @@ def gemma_cpu_baseline(dec, ctx_len, seed):
                       f"(bf16-equivalent bytes of that layer / time)"}
 
 
+def bench_agentic(args):
+    """Agentic sessions on the 34-layer Gemma-3-4B-shaped decoder through the
+    engine (prefix cache, chunked prefill, decode steps replayed as HIP graphs):
+    a shared reference prefix is cached first; S sessions then each run T
+    turns: the first prefills a prompt that starts with the shared prefix, each
+    later turn appends new user tokens to the retained conversation (its pages
+    are found in the prefix cache), and every turn generates a fixed number of
+    tokens greedily.  A session waits a fixed user delay between turns; the
+    clock is simulated (engine time is measured, the delay is added, nothing
+    sleeps).  Reports session time and the share of engine time spent in
+    decode-only steps."""
+    torch, bi, synth = _torch_env()
+    from deterministic_paged_attention_amd.decoder import Decoder, DecoderShape
+    from deterministic_paged_attention_amd.engine import Engine
+    from synth.workloads import decoder_weights
+    s = DecoderShape()
+    S, T = args.sessions, args.turns
+    shared_len, prompt_len, turn_in, turn_out = args.shared_tokens, args.prompt_tokens, args.turn_input, args.turn_output
+    delay = args.user_delay
+    w = decoder_weights(s.layers, s.hidden, s.q_heads, s.kv_heads, s.head_dim, s.ffn, s.vocab, seed=args.seed + 90)
+    dec = Decoder(s, w)
+    ctx_max = prompt_len + T * (turn_in + turn_out) + 64
+    num_pages = (shared_len + S * ctx_max) // s.page_size + 256
+    eng = Engine(dec, num_pages=num_pages, budget=args.prefill_budget, check_writes=False, graphs=True,
+                 record_logits=False)
+    V = s.vocab
+    shared = synth.uniform_ints(shared_len, 0, V - 1, args.seed + 91)
+    # cache the shared prefix: one request over it (its pages are registered as they fill)
+    eng.add(-1, shared + [0], 1)
+    while eng.step():
+        pass
+    torch.cuda.synchronize()
+    conv = {k: shared + synth.uniform_ints(prompt_len - shared_len, 0, V - 1, args.seed + 100 + k) for k in range(S)}
+    ready = {k: 0.0 for k in range(S)}       # simulated time the session's next turn arrives
+    turn = {k: 0 for k in range(S)}
+    active = {}                              # request id -> session
+    clock = 0.0
+    t_decode = t_mixed = 0.0
+    n_decode_steps = n_mixed_steps = 0
+    generated = 0
+    done_at = {}
+    rid = 0
+    while len(done_at) < S:
+        for k in range(S):
+            if k not in done_at and k not in active.values() and ready[k] <= clock:
+                eng.add(rid, conv[k], turn_out)
+                active[rid] = k
+                rid += 1
+        if not active:
+            clock = min(ready[k] for k in range(S) if k not in done_at)
+            continue
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        eng.step()
+        torch.cuda.synchronize()
+        dt = time.perf_counter() - t0
+        clock += dt
+        if eng.last_step_decode_only:
+            t_decode += dt
+            n_decode_steps += 1
+        else:
+            t_mixed += dt
+            n_mixed_steps += 1
+        for r_id in [r for r in active if r in eng.finished]:
+            k = active.pop(r_id)
+            req = eng.finished[r_id]
+            generated += len(req.tokens)
+            turn[k] += 1
+            conv[k] = conv[k] + req.tokens
+            print(json.dumps({"progress": {"session": k, "turn": turn[k], "clock_s": round(clock, 3)}}),
+                  file=sys.stderr, flush=True)
+            if turn[k] == T:
+                done_at[k] = clock
+            else:
+                conv[k] = conv[k] + synth.uniform_ints(turn_in, 0, V - 1, args.seed + 1000 * k + turn[k])
+                ready[k] = clock + delay
+    engine_time = t_decode + t_mixed
+    reused = sum(r.reused_pages for r in eng.finished.values() if r.rid >= 0)
+    print(json.dumps({
+        "metric": "agentic sessions: decode share of engine time and output tokens/s", "value": round(generated / engine_time, 1),
+        "unit": "output tokens/s (engine time)", "n_gpus": 1, "steps": eng.steps, "warmup": 0,
+        "ms_per_step": round(engine_time / max(eng.steps, 1) * 1e3, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "agentic sessions on a gemma-3-4b-shaped decoder (random init) through the engine",
+                   "sessions": S, "turns": T, "shared_prefix_tokens": shared_len, "first_prompt_tokens": prompt_len,
+                   "turn_input_tokens": turn_in, "turn_output_tokens": turn_out, "user_delay_s": delay,
+                   "prefill_budget": args.prefill_budget},
+        "session_time_s": round(max(done_at.values()), 3), "engine_time_s": round(engine_time, 3),
+        "decode_share_of_engine_time": round(t_decode / engine_time, 4),
+        "decode_steps": n_decode_steps, "steps_with_prefill": n_mixed_steps,
+        "decode_ms_per_step": round(t_decode / max(n_decode_steps, 1) * 1e3, 3),
+        "generated_tokens": generated, "prefix_pages_reused": reused, "graph_replays": eng.graph_replays,
+        "graphs_captured": len(eng._graphs), "cache_stats": list(eng.cache.stats())}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="decode", choices=["decode", "decode-sweep", "gemm", "prefill", "gemma"])
+    ap.add_argument("--workload", default="decode",
+                    choices=["decode", "decode-sweep", "gemm", "prefill", "gemma", "agentic"])
+    ap.add_argument("--sessions", type=int, default=4)
+    ap.add_argument("--turns", type=int, default=6)
+    ap.add_argument("--shared-tokens", type=int, default=8192)
+    ap.add_argument("--prompt-tokens", type=int, default=16384)
+    ap.add_argument("--turn-input", type=int, default=256)
+    ap.add_argument("--turn-output", type=int, default=768)
+    ap.add_argument("--user-delay", type=float, default=0.5)
+    ap.add_argument("--prefill-budget", type=int, default=2048)
     ap.add_argument("--batch", type=int, default=256)
     ap.add_argument("--seed", type=int, default=2000)
     ap.add_argument("--cpu-sample", type=int, default=256)
@@ -700,7 +807,7 @@ def main():
               f"(asked for --gpus {args.gpus}, WORLD_SIZE {world}).", file=sys.stderr)
         sys.exit(2)
     {"decode": bench_decode, "decode-sweep": bench_decode_sweep, "gemm": bench_gemm, "prefill": bench_prefill,
-     "gemma": bench_gemma}[args.workload](args)
+     "gemma": bench_gemma, "agentic": bench_agentic}[args.workload](args)
 
 
 if __name__ == "__main__":

@@ -53,9 +53,38 @@ class Request:
         return list(zip(self.tokens, self.logit_digests))
 
 
+class _DecodeGraph:
+    """A decode step (B sequences, one new token each) captured as one HIP
+    graph over static input buffers; page tables up to `stride` entries and
+    contexts up to stride * page_size tokens replay it with new contents."""
+
+    def __init__(self, dec, kv, B: int, stride: int, page_size: int):
+        dev = "cuda"
+        self.B, self.stride = B, stride
+        self.ids = torch.zeros(B, dtype=torch.int32, device=dev)
+        self.pt = torch.full((B, stride), -1, dtype=torch.int32, device=dev)
+        self.sl = torch.ones(B, dtype=torch.int32, device=dev)
+        self.qsl = torch.arange(B + 1, dtype=torch.int32, device=dev)
+        self.rows = torch.arange(B, dtype=torch.int32, device=dev)
+        self.graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(self.graph):
+            self.logits = dec.step(self.ids, kv, self.pt, self.sl, self.qsl, stride * page_size,
+                                   logit_rows=self.rows)
+            self.tokens = bi_argmax(self.logits)
+
+    def run(self, ids, pt_host, sls):
+        pad = np.full((self.B, self.stride), -1, dtype=np.int32)
+        pad[:, :pt_host.shape[1]] = pt_host
+        self.ids.copy_(torch.tensor(ids, dtype=torch.int32))
+        self.pt.copy_(torch.from_numpy(pad))
+        self.sl.copy_(torch.tensor(sls, dtype=torch.int32))
+        self.graph.replay()
+        return self.logits, self.tokens
+
+
 class Engine:
     def __init__(self, decoder, num_pages: int, budget: int, check_writes: bool = True,
-                 hash_bits: int = 64):
+                 hash_bits: int = 64, graphs: bool = False, record_logits: bool = True):
         self.dec = decoder
         self.P = decoder.shape.page_size
         self.num_pages = num_pages
@@ -63,10 +92,15 @@ class Engine:
         self.kv = decoder.new_caches(num_pages)
         self.budget = budget
         self.check_writes = check_writes
+        self.graphs = graphs
+        self.record_logits = record_logits
+        self._graphs: Dict[tuple, _DecodeGraph] = {}
         self.waiting: deque = deque()
         self.running: List[Request] = []
         self.finished: Dict[int, Request] = {}
         self.steps = 0
+        self.graph_replays = 0
+        self.last_step_decode_only = False
 
     def add(self, rid: int, prompt: List[int], max_new: int):
         if not prompt or max_new < 1:
@@ -126,19 +160,33 @@ class Engine:
         if self.check_writes:
             slots = [r.pages[p // self.P] * self.P + p % self.P for r, n in batch for p in range(r.cached, r.cached + n)]
             bi_check_write_plan(slots, self.cache.writable(), self.num_pages, self.P)
-        logits = self.dec.step(torch.tensor(ids, dtype=torch.int32, device=dev), self.kv,
-                               torch.from_numpy(pt).to(dev), torch.tensor(sls, dtype=torch.int32, device=dev),
-                               torch.tensor(qsl, dtype=torch.int32, device=dev), max(sls),
-                               logit_rows=torch.tensor(rows, dtype=torch.int32, device=dev) if rows else None)
-        sampled = bi_argmax(logits).cpu().tolist() if rows else []
-        host_logits = logits.cpu().numpy() if rows else None
+        decode_only = all(n == 1 for _, n in batch) and len(rows) == len(batch)
+        self.last_step_decode_only = decode_only
+        # Decode steps replay a captured graph once their shape bucket has been
+        # seen (the first step of a bucket runs eagerly); everything else runs eagerly.
+        bucket = (len(batch), -(-stride // 16) * 16)
+        g = self._graphs.get(bucket) if (self.graphs and decode_only) else None
+        if g is not None:
+            logits, toks = g.run(ids, pt, sls)
+            self.graph_replays += 1
+        else:
+            logits = self.dec.step(torch.tensor(ids, dtype=torch.int32, device=dev), self.kv,
+                                   torch.from_numpy(pt).to(dev), torch.tensor(sls, dtype=torch.int32, device=dev),
+                                   torch.tensor(qsl, dtype=torch.int32, device=dev), max(sls),
+                                   logit_rows=torch.tensor(rows, dtype=torch.int32, device=dev) if rows else None)
+            toks = bi_argmax(logits) if rows else None
+            if self.graphs and decode_only:
+                self._graphs[bucket] = _DecodeGraph(self.dec, self.kv, bucket[0], bucket[1], self.P)
+        sampled = toks.cpu().tolist() if rows else []
+        host_logits = logits.cpu().numpy() if (rows and self.record_logits) else None
         k = 0
         for r, n in batch:
             r.cached += n
             if r.cached == len(r.history):
                 tok = int(sampled[k])
                 r.tokens.append(tok)
-                r.logit_digests.append(hashlib.sha256(host_logits[k].tobytes()).hexdigest())
+                if host_logits is not None:
+                    r.logit_digests.append(hashlib.sha256(host_logits[k].tobytes()).hexdigest())
                 r.history.append(tok)
                 k += 1
             self._register_full_pages(r)

@@ -68,7 +68,7 @@ def _arrivals(order, gaps, prompts, max_new):
 
 def test_per_request_views_agree_across_schedules_pools_and_cache_hits(decoder):
     prompts = _prompts()
-    max_new = 5
+    max_new = 6
     runs = {}
     # A: staggered arrivals (later requests hit the cached system prefix), budget 256
     eA = Engine(decoder, num_pages=600, budget=256)
@@ -79,6 +79,11 @@ def test_per_request_views_agree_across_schedules_pools_and_cache_hits(decoder):
     # C: one request at a time on a pool so small that cached pages must be evicted
     eC = Engine(decoder, num_pages=40, budget=512)
     runs["C"] = eC.run(arrivals=_arrivals([2, 0, 3, 1, 4, 5, 6, 7], [0, 8, 8, 8, 8, 8, 8, 8], prompts, max_new))
+    # E: as A, with decode steps replayed from captured HIP graphs (many replays per graph,
+    # eager prefill steps between them)
+    eE = Engine(decoder, num_pages=600, budget=256, graphs=True)
+    runs["E"] = eE.run(arrivals=_arrivals([0, 6, 1, 2, 3, 7, 4, 5], [0, 0, 4, 0, 0, 0, 5, 0], prompts, max_new))
+    assert len(eE._graphs) >= 1 and eE.graph_replays >= 3
     # D: every request alone, no sharing possible (fresh engine each)
     runs["D"] = {}
     for rid in prompts:
@@ -90,7 +95,7 @@ def test_per_request_views_agree_across_schedules_pools_and_cache_hits(decoder):
         for rid, r in fin.items():
             assert len(r.tokens) == max_new, (name, rid)
     ref = runs["D"]
-    for name in ("A", "B", "C"):
+    for name in ("A", "B", "C", "E"):
         for rid in prompts:
             assert runs[name][rid].view() == ref[rid].view(), (name, rid)
     for name in runs:
