@@ -101,11 +101,21 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
                                            0x00020000);
 }
 
+// Split launches (ksplit_len > 0, grid y = number of splits): workgroup row y
+// multiplies the K range [y*ksplit_len, min((y+1)*ksplit_len, K)) into fp32
+// partial y (c + y*M*N, row stride ldc), all splits at once.
 template <int BM, int BN, int WM, int BK, int STAGES>
 __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
                                                         int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
-                                                        int64_t N, int64_t K) {
+                                                        int64_t N, int64_t K, int64_t ksplit_len) {
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts and buffer-to-LDS copies exist on the GPU only
+  if (ksplit_len > 0) {
+    const int64_t k0 = (int64_t)blockIdx.y * ksplit_len;
+    a += k0;
+    w += k0;
+    K = min(ksplit_len, K - k0);
+    c = reinterpret_cast<float*>(c) + (int64_t)blockIdx.y * M * N;
+  }
   constexpr int WN = 4 / WM;
   constexpr int MB = BM / WM / 16;            // 16-row m blocks per wave
   constexpr int NB = BN / WN / 16;            // 16-row n blocks per wave
@@ -246,13 +256,16 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
 #endif
 }
 
+// nsplit > 1: split launch over K ranges of ksplit_len into fp32 partials
+// (see the kernel).
 template <int BM, int BN, int WM, int BK, int STAGES>
 hipError_t ring_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
-                       int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+                       int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream, int64_t ksplit_len,
+                       int64_t nsplit) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t groups = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, BK, STAGES>), dim3((unsigned)groups), dim3(256), 0, stream, a, lda,
-                     w, ldw, c, ldc, out_kind, M, N, K);
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, BK, STAGES>), dim3((unsigned)groups, (unsigned)nsplit), dim3(256),
+                     0, stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K, nsplit > 1 ? ksplit_len : (int64_t)0);
   return hipGetLastError();
 }
 
@@ -270,15 +283,20 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
 
 }  // namespace
 
-hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
-                       int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
-  if (M == 0 || N == 0) return hipSuccess;
+namespace {
+// Tile configuration by (M, N); with nsplit > 1 the K ranges of ksplit_len
+// run as one launch into fp32 partials.  N here is the partial's width.
+hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
+                            int out_kind, int64_t M, int64_t N, int64_t K, int64_t ksplit_len, int64_t nsplit,
+                            hipStream_t stream) {
   // The mapping follows M (and N, which every call of a given weight
   // shares); the arithmetic of every output element does not.  Tile shape,
   // slice width and ring depth come from a measured sweep on MI355X: skinny
   // M wants long contiguous row runs and many slices in flight; larger M
   // wants larger tiles to cut operand re-reads.
-  auto L = [&](auto kernel_cfg) { return kernel_cfg(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream); };
+  auto L = [&](auto kernel_cfg) {
+    return kernel_cfg(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream, ksplit_len, nsplit);
+  };
   if (M <= 32) {
     if (N >= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
     return L(ring_launch<32, 32, 2, 512, 2>);
@@ -302,18 +320,21 @@ hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_
   return L(ring_launch<128, 128, 2, 64, 4>);
 }
 
+}  // namespace
+
+hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
+                       int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
+  if (M == 0 || N == 0) return hipSuccess;
+  return launch_gemm_impl(a, lda, w, ldw, c, ldc, out_kind, M, N, K, 0, 1, stream);
+}
+
 hipError_t launch_gemm_splitk(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, float* partial,
                               int64_t M, int64_t N, int64_t K, int32_t k_splits, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   // Split z multiplies the K range [z*kc, (z+1)*kc) with the product kernel
-  // into fp32 partial[z]; the tile configuration is the product's for (M, N).
-  const int64_t kc = K / k_splits;
-  for (int32_t z = 0; z < k_splits; ++z) {
-    const hipError_t e = launch_gemm(a + z * kc, lda, w + z * kc, ldw, partial + (int64_t)z * M * N, N, 1, M, N, kc,
-                                     stream);
-    if (e != hipSuccess) return e;
-  }
-  return hipSuccess;
+  // into fp32 partial[z]; all splits in one launch, the tile configuration
+  // being the product's for (M, N).
+  return launch_gemm_impl(a, lda, w, ldw, partial, N, 1, M, N, K, K / k_splits, k_splits, stream);
 }
 
 hipError_t launch_gemm_splitk_reduce(const float* partial, int32_t k_splits, int64_t M, int64_t N, void* c,
@@ -323,5 +344,6 @@ hipError_t launch_gemm_splitk_reduce(const float* partial, int32_t k_splits, int
                      k_splits, M, N, c, ldc, out_kind);
   return hipGetLastError();
 }
+
 
 }  // namespace bi
