@@ -261,7 +261,7 @@ def bench_decode(args):
                    "hidden": HIDDEN, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(B),
-                     "kernel": "attn_split_kernel<128>", "algorithmic_bytes_per_launch": sb,
+                     "kernel": "attn_split_kernel<128, 1>", "algorithmic_bytes_per_launch": sb,
                      "avg_launch_us": round(split_us, 2)},
         "cpu_baseline": cpu,
         "attention_gbps": round(attn_gbps, 2),
