@@ -132,10 +132,6 @@ def bench_decode(args):
     w_o = synth.normal_bf16_device((HIDDEN, HQ * D), args.seed + 13, std=0.02)
     torch.cuda.synchronize()
 
-    cpu = None
-    if not args.no_cpu_baseline:
-        cpu = cpu_baseline(wl, min(args.cpu_sample, B))
-
     xn = torch.empty((B, HIDDEN), dtype=torch.bfloat16, device=dev)
     qkv = torch.empty((B, QKV_N), dtype=torch.bfloat16, device=dev)
     q = qkv[:, : HQ * D].view(B, HQ, D)
@@ -233,6 +229,12 @@ def bench_decode(args):
         splitk = {"invariant_us": round(t_inv, 2), "splitk_us": round(per_n[best], 2), "splitk_num_splits": best,
                   "heuristic_num_splits": heur, "splitk_us_by_num_splits": {str(n): round(v, 2) for n, v in per_n.items()},
                   "overhead": round(t_inv / per_n[best] - 1.0, 4)}
+
+    # The oracle runs after the GPU timing: its BLAS threads keep spinning for a
+    # while after each call and would delay the host launching the timed steps.
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, min(args.cpu_sample, B))
 
     if args.copy_calibration_mib:
         n = args.copy_calibration_mib * (1 << 20) // 2

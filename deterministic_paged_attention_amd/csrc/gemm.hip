@@ -14,13 +14,15 @@
 // lane l supplies k-slots 8*(l>>4) .. 8*(l>>4)+7 of the 32-wide K step, both
 // operands K-major as stored.
 //
-// The product mapping, gemm_ring_kernel<BM, BN, WM, BK, STAGES>: a workgroup
-// owns a BM x BN tile and streams BK-wide K slices of both operands into an
-// LDS ring with direct-to-LDS buffer loads.  The tile configuration is chosen
-// from M and N; every configuration performs the same per-element instruction
-// sequence (same instruction, same K steps in the same order, same k-slot
-// layout per lane group), so which one runs never changes a bit of any
-// output row.
+// The product mappings: gemm_ring_kernel<BM, BN, WM, BK, STAGES> (a
+// workgroup owns a BM x BN tile and streams BK-wide K slices of both operands
+// into an LDS ring with direct-to-LDS buffer loads) and, for M <= 16,
+// gemm_skinny_kernel<STAGES> (a workgroup owns 16 weight rows; three waves
+// stream them through the ring while one wave computes).  The kernel and its
+// configuration are chosen from M and N; every choice performs the same
+// per-element instruction sequence (same instruction, same K steps in the
+// same order, same k-slot layout per lane group), so which one runs never
+// changes a bit of any output row.
 //
 // The split-K comparator (measurement only) runs the same kernel over K
 // sub-ranges into fp32 partials and sums them in split order afterwards, so
@@ -125,6 +127,11 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
   constexpr int IPW = (G + 3) / 4;            // per slice for waves 0 .. G%4-1 (all if G%4 == 0)
   constexpr int STAGE = (BM + BN) * BK;       // elements per stage
   constexpr int SPS = BK / 32;                // MFMA K steps per slice
+  // K steps whose fragments are read together: all of a slice for the small
+  // tiles of skinny M (where one LDS round trip per step would dominate),
+  // one step at a time for the large, register-heavy tiles.
+  constexpr int GK = (NB + MB) <= 4 ? (SPS < 32 / (NB + MB) ? SPS : 32 / (NB + MB)) : 1;
+  static_assert(SPS % GK == 0, "K-step groups tile the slice");
   static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "tile shape");
   static_assert((BK == 64 || BK == 128 || BK == 256 || BK == 512) && (BM + BN) % RPI == 0, "slice shape");
   static_assert(STAGES >= 2, "ring depth");
@@ -198,26 +205,55 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     const uint32_t sa = lds_base + (uint32_t)((s % STAGES) * STAGE * 2);
     const uint32_t sw = sa + BM * BK * 2;
     const int ksteps = (int)min<int64_t>(SPS, nsteps - SPS * s);  // fewer only on a ragged final slice
-    // One K step at a time: its fragments are read and waited for in full
-    // before its MFMAs.  (The reads are not prefetched a step ahead: the
-    // compiler does not know these registers fill asynchronously and may copy
-    // them before the wait.)
-    for (int ks = 0; ks < ksteps; ++ks) {
-      const uint32_t cs = (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16);
-      u32x4 fw[NB], fa[MB];
+    // Full slices: K steps in groups of GK; the fragments of a group are read
+    // together and waited for in full before its MFMAs, which run in step
+    // order (one LDS round trip per group, straight-line code).  A ragged final
+    // slice goes one step at a time.  The reads are not prefetched a group
+    // ahead: the compiler does not know these registers fill asynchronously
+    // and may copy them before the wait.
+    if (ksteps == SPS) {
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
-        fw[i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
+      for (int kg = 0; kg < SPS; kg += GK) {
+        u32x4 fw[GK * NB], fa[GK * MB];
 #pragma unroll
-      for (int j = 0; j < MB; ++j)
-        fa[j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
-      lds_wait<0>(fw, fa);
+        for (int q = 0; q < GK; ++q) {
+          const uint32_t cs = (uint32_t)(((4 * (kg + q) + g4) ^ (r & 7)) * 16);
 #pragma unroll
-      for (int i = 0; i < NB; ++i)
+          for (int i = 0; i < NB; ++i)
+            fw[q * NB + i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            fa[q * MB + j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
+        }
+        lds_wait<0>(fw, fa);
+#pragma unroll
+        for (int q = 0; q < GK; ++q)
+#pragma unroll
+          for (int i = 0; i < NB; ++i)
+#pragma unroll
+            for (int j = 0; j < MB; ++j)
+              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[q * NB + i]),
+                                                                 __builtin_bit_cast(bf16x8, fa[q * MB + j]),
+                                                                 acc[i][j], 0, 0, 0);
+      }
+    } else {
+      for (int ks = 0; ks < ksteps; ++ks) {
+        const uint32_t cs = (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16);
+        u32x4 fw[NB], fa[MB];
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+          fw[i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
 #pragma unroll
         for (int j = 0; j < MB; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[i]),
-                                                             __builtin_bit_cast(bf16x8, fa[j]), acc[i][j], 0, 0, 0);
+          fa[j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
+        lds_wait<0>(fw, fa);
+#pragma unroll
+        for (int i = 0; i < NB; ++i)
+#pragma unroll
+          for (int j = 0; j < MB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[i]),
+                                                               __builtin_bit_cast(bf16x8, fa[j]), acc[i][j], 0, 0, 0);
+      }
     }
   }
   wait_vmcnt<0>();                           // drain the trailing (empty) copies
@@ -256,6 +292,170 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
 #endif
 }
 
+// ---------------------------------------------------------------------------
+// Skinny mapping (M <= 16): a workgroup owns 16 rows of w (one output block).
+// Waves 1..3 stream those rows through an LDS ring of STAGES 512-wide slices
+// (one 1 KiB contiguous run of one row per copy instruction; STAGES - 1
+// slices in flight), wave 0 loads the rows of a straight into registers one
+// slice ahead and runs the MFMAs — the same per-element instruction sequence
+// as the ring mapping (A operand = 16 rows of w, B operand = the rows of a,
+// k-slots 8*(lane>>4) .. +7 of each 32-wide step, increasing K).  Rows of a
+// past M are not loaded: they only feed output columns that are discarded.
+// ---------------------------------------------------------------------------
+constexpr int kSkinnyBK = 512;
+constexpr int kSkinnyStages = 8;
+
+template <int STAGES>
+__global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
+                                                          int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
+                                                          int64_t N, int64_t K, int64_t ksplit_len) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  constexpr int BK = kSkinnyBK;
+  constexpr int SPS = BK / 32;                // MFMA K steps per slice
+  constexpr int STAGE = 16 * BK;              // elements per stage: 16 rows x BK
+  __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
+  if (ksplit_len > 0) {
+    const int64_t k0 = (int64_t)blockIdx.y * ksplit_len;
+    a += k0;
+    w += k0;
+    K = min(ksplit_len, K - k0);
+    c = reinterpret_cast<float*>(c) + (int64_t)blockIdx.y * M * N;
+  }
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int r = lane & 15, g4 = lane >> 4;
+  const int64_t n0 = (int64_t)blockIdx.x * 16;
+  if (n0 >= N) return;
+  const int64_t nsteps = K / 32;
+  const int64_t nslices = (nsteps + SPS - 1) / SPS;
+  const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
+
+  if (wave != 0) {
+    // Copy waves: wave 1 rows 0..5, wave 2 rows 6..10, wave 3 rows 11..15.
+    const int rb = wave == 1 ? 0 : (wave == 2 ? 6 : 11);
+    const int cnt = wave == 1 ? 6 : 5;
+    const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w + n0 * ldw, min<int64_t>(16, N - n0), ldw, K);
+    const __amdgpu_buffer_rsrc_t rzero = rows_rsrc(w, 0, ldw, K);
+    uint32_t voff[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) {
+      const int row = rb + i;
+      voff[i] = (uint32_t)(row * ldw * 2 + ((lane ^ (row & 7)) * 16));   // chunk c of row R lands in slot c ^ (R & 7)
+    }
+    auto issue = [&](int64_t s) {
+      const int st = (int)(s % STAGES);
+      const bool live = s < nslices;
+#pragma unroll
+      for (int i = 0; i < 6; ++i) {
+        if (i >= cnt) break;                  // wave-uniform
+        lds_void* dst = (lds_void*)(lds + st * STAGE + (rb + i) * BK);
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rw : rzero, dst, 16, voff[i] + (uint32_t)(s * BK * 2), 0,
+                                                 0, 0);
+      }
+    };
+#pragma unroll
+    for (int p = 0; p < STAGES - 1; ++p) issue(p);
+    for (int64_t s = 0; s < nslices; ++s) {
+      if (cnt == 6) wait_vmcnt<6 * (STAGES - 2)>();
+      else wait_vmcnt<5 * (STAGES - 2)>();
+      __builtin_amdgcn_s_barrier();           // slice s is in LDS; slice s-1 is no longer read
+      issue(s + STAGES - 1);
+    }
+    wait_vmcnt<0>();
+    return;
+  }
+
+  // Compute wave.  B operand: row r of a, k-slots 8*g4 .. 8*g4+7 of each step,
+  // read through a descriptor ending at the last valid element of a: rows
+  // past M (and anything past the end) read as zero without memory traffic;
+  // steps past K on the last slice read data no MFMA uses.  The loads are
+  // unconditional so that their waits stay counted, not serialized.
+  const bool m_ok = r < M;
+  const __amdgpu_buffer_rsrc_t ra = rows_rsrc(a, min<int64_t>(16, M), lda, K);
+  const uint32_t aoff = (uint32_t)(r * lda * 2 + 16 * g4);
+  u32x4 af[2][SPS];
+  auto load_a = [&](int64_t s, u32x4 (&dst)[SPS]) {
+#pragma unroll
+    for (int ks = 0; ks < SPS; ++ks)
+      dst[ks] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                                              ra, aoff + (uint32_t)((s * BK + 32 * ks) * 2), 0, 0));
+  };
+  f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  auto slice = [&](int64_t s, u32x4 (&cur)[SPS], u32x4 (&nxt)[SPS]) {
+    load_a(s + 1, nxt);                      // next slice's rows of a, in flight during this one
+    __builtin_amdgcn_s_barrier();            // slice s of w is in LDS
+    const uint32_t sw = lds_base + (uint32_t)((s % STAGES) * STAGE * 2);
+    const int ksteps = (int)min<int64_t>(SPS, nsteps - SPS * s);
+    // A full slice reads all of its w fragments at once (one LDS round trip
+    // per slice, straight-line code), then runs its MFMAs in step order; a
+    // ragged final slice goes one step at a time.
+    if (ksteps == SPS) {
+      u32x4 fw[SPS];
+#pragma unroll
+      for (int ks = 0; ks < SPS; ++ks)
+        fw[ks] = lds_read16(sw + (uint32_t)(r * BK * 2) + (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16));
+      lds_wait<0>(fw, cur);
+#pragma unroll
+      for (int ks = 0; ks < SPS; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[ks]),
+                                                      __builtin_bit_cast(bf16x8, cur[ks]), acc, 0, 0, 0);
+    } else {
+#pragma unroll
+      for (int ks = 0; ks < SPS; ++ks) {    // static register indices; the guard is wave-uniform
+        if (ks < ksteps) {
+          u32x4 fw[1] = {lds_read16(sw + (uint32_t)(r * BK * 2) + (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16))};
+          u32x4 fa[1] = {cur[ks]};
+          lds_wait<0>(fw, fa);
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[0]),
+                                                        __builtin_bit_cast(bf16x8, fa[0]), acc, 0, 0, 0);
+        }
+      }
+    }
+  };
+  load_a(0, af[0]);
+  int64_t s = 0;
+  for (; s + 1 < nslices; s += 2) {
+    slice(s, af[0], af[1]);
+    slice(s + 1, af[1], af[0]);
+  }
+  if (s < nslices) slice(s, af[0], af[1]);
+
+  // Lane holds C^T[n0 + 4*g4 + i][r].
+  if (!m_ok) return;
+  const int64_t nb = n0 + 4 * g4;
+  if (out_kind == 1) {
+    float* cp = reinterpret_cast<float*>(c) + (int64_t)r * ldc + nb;
+    if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 15) == 0)) {
+      *reinterpret_cast<f32x4*>(cp) = acc;
+    } else {
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < N) cp[e] = acc[e];
+    }
+  } else {
+    uint16_t* cp = reinterpret_cast<uint16_t*>(c) + (int64_t)r * ldc + nb;
+    bf16x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) o[e] = (__bf16)acc[e];
+    if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 7) == 0)) {
+      *reinterpret_cast<bf16x4*>(cp) = o;
+    } else {
+      const u32x2 bits = __builtin_bit_cast(u32x2, o);
+      for (int e = 0; e < 4; ++e)
+        if (nb + e < N) cp[e] = (uint16_t)((e & 1) ? (bits[e >> 1] >> 16) : (bits[e >> 1] & 0xffffu));
+    }
+  }
+#endif
+}
+
+template <int STAGES>
+hipError_t skinny_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
+                         int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream, int64_t ksplit_len,
+                         int64_t nsplit) {
+  hipLaunchKernelGGL(gemm_skinny_kernel<STAGES>, dim3((unsigned)((N + 15) / 16), (unsigned)nsplit), dim3(256), 0,
+                     stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K, nsplit > 1 ? ksplit_len : (int64_t)0);
+  return hipGetLastError();
+}
+
 // nsplit > 1: split launch over K ranges of ksplit_len into fp32 partials
 // (see the kernel).
 template <int BM, int BN, int WM, int BK, int STAGES>
@@ -290,34 +490,41 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
                             int out_kind, int64_t M, int64_t N, int64_t K, int64_t ksplit_len, int64_t nsplit,
                             hipStream_t stream) {
   // The mapping follows M (and N, which every call of a given weight
-  // shares); the arithmetic of every output element does not.  Tile shape,
-  // slice width and ring depth come from a measured sweep on MI355X: skinny
-  // M wants long contiguous row runs and many slices in flight; larger M
-  // wants larger tiles to cut operand re-reads.
+  // shares); the arithmetic of every output element does not.  Kernel, tile
+  // shape, slice width and ring depth come from a measured sweep on MI355X:
+  // skinny M wants long contiguous weight-row runs, many slices in flight and
+  // few LDS round trips per slice; larger M wants larger tiles to cut operand
+  // re-reads.
   auto L = [&](auto kernel_cfg) {
     return kernel_cfg(a, lda, w, ldw, c, ldc, out_kind, M, N, K, stream, ksplit_len, nsplit);
   };
+  if (M <= 16) {
+    if (N <= 8192 || (N >= 16384 && M <= 4)) return L(skinny_launch<4>);
+    if (N < 16384) return L(ring_launch<32, 32, 2, 256, 2>);
+    return L(ring_launch<64, 64, 2, 128, 2>);
+  }
   if (M <= 32) {
-    if (N >= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
-    return L(ring_launch<32, 32, 2, 512, 2>);
+    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 4>);
+    if (N < 16384) return L(ring_launch<32, 64, 2, 128, 5>);
+    return L(ring_launch<64, 64, 2, 128, 2>);
   }
   if (M <= 64) {
-    if (N >= 16384) return L(ring_launch<64, 128, 2, 128, 3>);
-    if (N >= 8192) return L(ring_launch<64, 64, 2, 128, 4>);
-    return L(ring_launch<32, 32, 2, 256, 4>);
+    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 4>);
+    if (N < 16384) return L(ring_launch<64, 64, 2, 128, 4>);
+    return L(ring_launch<64, 128, 2, 128, 3>);
   }
   if (M <= 128) {
-    if (N >= 16384) return L(ring_launch<128, 128, 2, 64, 4>);
-    if (N >= 8192) return L(ring_launch<64, 64, 2, 128, 2>);
-    return L(ring_launch<32, 32, 2, 256, 2>);
+    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
+    if (N < 16384) return L(ring_launch<64, 64, 2, 128, 2>);
+    return L(ring_launch<128, 128, 2, 64, 4>);
   }
   if (M <= 256) {
-    if (N >= 16384) return L(ring_launch<256, 128, 4, 64, 3>);
-    if (N >= 8192) return L(ring_launch<128, 128, 2, 64, 4>);
-    return L(ring_launch<64, 64, 2, 128, 4>);
+    if (N <= 8192) return L(ring_launch<64, 64, 2, 128, 4>);
+    if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4>);
+    return L(ring_launch<256, 128, 4, 64, 3>);
   }
-  if (N >= 8192) return L(ring_launch<256, 128, 4, 64, 3>);
-  return L(ring_launch<128, 128, 2, 64, 4>);
+  if (N <= 8192) return L(ring_launch<128, 128, 2, 64, 4>);
+  return L(ring_launch<256, 128, 4, 64, 3>);
 }
 
 }  // namespace

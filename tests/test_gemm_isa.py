@@ -26,7 +26,7 @@ def _build_module():
 
 
 def _kernels(asm: str):
-    for m in re.finditer(r"^(_Z\S*gemm_ring_kernel\S*?):[^\n]*\n(.*?)^\.Lfunc_end", asm, re.S | re.M):
+    for m in re.finditer(r"^(_Z\S*gemm_(?:ring|skinny)_kernel\S*?):[^\n]*\n(.*?)^\.Lfunc_end", asm, re.S | re.M):
         yield m.group(1), m.group(2)
 
 
