@@ -42,7 +42,7 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 // ---------------------------------------------------------------------------
 // LDS ring mapping.
 //
-// A workgroup (four waves) owns a BM x BN output tile.  K is consumed in
+// A workgroup (NW = four or eight waves) owns a BM x BN output tile.  K is consumed in
 // BK-wide slices; slice s of both operands is copied straight from global
 // memory into LDS stage s % STAGES by buffer loads that write LDS directly
 // (each wave instruction moves 1 KiB: 512/BK rows x 2*BK bytes; lane i of it
@@ -106,8 +106,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint16_t* base
 // Split launches (ksplit_len > 0, grid y = number of splits): workgroup row y
 // multiplies the K range [y*ksplit_len, min((y+1)*ksplit_len, K)) into fp32
 // partial y (c + y*M*N, row stride ldc), all splits at once.
-template <int BM, int BN, int WM, int BK, int STAGES>
-__global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
+template <int BM, int BN, int WM, int BK, int STAGES, int NW = 4>
+__global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
                                                         int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
                                                         int64_t N, int64_t K, int64_t ksplit_len) {
 #if defined(__HIP_DEVICE_COMPILE__)  // LDS address-space casts and buffer-to-LDS copies exist on the GPU only
@@ -118,13 +118,13 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     K = min(ksplit_len, K - k0);
     c = reinterpret_cast<float*>(c) + (int64_t)blockIdx.y * M * N;
   }
-  constexpr int WN = 4 / WM;
+  constexpr int WN = NW / WM;
   constexpr int MB = BM / WM / 16;            // 16-row m blocks per wave
   constexpr int NB = BN / WN / 16;            // 16-row n blocks per wave
   constexpr int CPR = BK / 8;                 // 16-byte chunks per row of a slice
   constexpr int RPI = 64 / CPR;               // rows moved by one copy instruction
   constexpr int G = (BM + BN) / RPI;          // copy instructions per slice
-  constexpr int IPW = (G + 3) / 4;            // per slice for waves 0 .. G%4-1 (all if G%4 == 0)
+  constexpr int IPW = (G + NW - 1) / NW;      // per slice for waves 0 .. G%NW-1 (all if G%NW == 0)
   constexpr int STAGE = (BM + BN) * BK;       // elements per stage
   constexpr int SPS = BK / 32;                // MFMA K steps per slice
   // K steps whose fragments are read together: all of a slice for the small
@@ -132,7 +132,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
   // one step at a time for the large, register-heavy tiles.
   constexpr int GK = (NB + MB) <= 4 ? (SPS < 32 / (NB + MB) ? SPS : 32 / (NB + MB)) : 1;
   static_assert(SPS % GK == 0, "K-step groups tile the slice");
-  static_assert(WM * WN == 4 && MB >= 1 && NB >= 1, "tile shape");
+  static_assert(WM * WN == NW && MB >= 1 && NB >= 1, "tile shape");
   static_assert((BK == 64 || BK == 128 || BK == 256 || BK == 512) && (BM + BN) % RPI == 0, "slice shape");
   static_assert(STAGES >= 2, "ring depth");
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
@@ -153,7 +153,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
   const int64_t n0 = (tile / nM) * BN;
 
   // Copy plan: instruction j of this wave moves rows RPI*gi .. RPI*gi+RPI-1
-  // of the stacked [a rows; w rows] slice, gi = wave + 4j, if gi < G.
+  // of the stacked [a rows; w rows] slice, gi = wave + NW*j, if gi < G.
   const __amdgpu_buffer_rsrc_t ra = rows_rsrc(a + m0 * lda, min<int64_t>(BM, M - m0), lda, K);
   const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w + n0 * ldw, min<int64_t>(BN, N - n0), ldw, K);
   const __amdgpu_buffer_rsrc_t rzero = rows_rsrc(a, 0, lda, K);
@@ -161,7 +161,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
   __amdgpu_buffer_rsrc_t rsj[IPW];
 #pragma unroll
   for (int j = 0; j < IPW; ++j) {
-    const int srow = RPI * (wave + 4 * j) + lane / CPR;    // row of the stacked slice
+    const int srow = RPI * (wave + NW * j) + lane / CPR;   // row of the stacked slice
     const bool is_a = srow < BM;
     const int row = is_a ? srow : srow - BM;
     const int chunk = (lane % CPR) ^ (srow & 7);           // logical chunk landing in this lane's slot
@@ -177,8 +177,8 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     const bool live = s < nslices;
 #pragma unroll
     for (int j = 0; j < IPW; ++j) {
-      if (G % 4 != 0 && wave + 4 * j >= G) break;  // wave-uniform
-      lds_void* dst = (lds_void*)(lds + st * STAGE + (wave + 4 * j) * 512);
+      if (G % NW != 0 && wave + NW * j >= G) break;  // wave-uniform
+      lds_void* dst = (lds_void*)(lds + st * STAGE + (wave + NW * j) * 512);
       __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rsj[j] : rzero, dst, 16,
                                                voff[j] + (uint32_t)(s * BK * 2), 0, 0, 0);
     }
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void gemm_ring_kernel(const uint16_t* a, int64
     // reads below are explicit ds_read instructions and the waits are ours:
     // this wave's copies of slice s are done (vmcnt), then everyone's are and
     // nobody still reads slice s-1 (barrier).
-    if (G % 4 == 0 || wave < G % 4) wait_vmcnt<IPW * (STAGES - 2)>();
+    if (G % NW == 0 || wave < G % NW) wait_vmcnt<IPW * (STAGES - 2)>();
     else wait_vmcnt<(IPW - 1) * (STAGES - 2)>();
     __builtin_amdgcn_s_barrier();
     issue(s + STAGES - 1);                   // into the stage slice s-1 used
@@ -458,14 +458,15 @@ hipError_t skinny_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int6
 
 // nsplit > 1: split launch over K ranges of ksplit_len into fp32 partials
 // (see the kernel).
-template <int BM, int BN, int WM, int BK, int STAGES>
+template <int BM, int BN, int WM, int BK, int STAGES, int NW = 4>
 hipError_t ring_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
                        int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream, int64_t ksplit_len,
                        int64_t nsplit) {
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   const int64_t groups = (tiles + kXcds - 1) / kXcds * kXcds;
-  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, BK, STAGES>), dim3((unsigned)groups, (unsigned)nsplit), dim3(256),
-                     0, stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K, nsplit > 1 ? ksplit_len : (int64_t)0);
+  hipLaunchKernelGGL((gemm_ring_kernel<BM, BN, WM, BK, STAGES, NW>), dim3((unsigned)groups, (unsigned)nsplit),
+                     dim3(64 * NW), 0, stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K,
+                     nsplit > 1 ? ksplit_len : (int64_t)0);
   return hipGetLastError();
 }
 
@@ -513,18 +514,23 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
     if (N < 16384) return L(ring_launch<64, 64, 2, 128, 4>);
     return L(ring_launch<64, 128, 2, 128, 3>);
   }
+  // Above M = 64, eight-wave workgroups (two waves per SIMD) let one wave's
+  // LDS reads overlap another's MFMAs.
   if (M <= 128) {
     if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
-    if (N < 16384) return L(ring_launch<64, 64, 2, 128, 2>);
-    return L(ring_launch<128, 128, 2, 64, 4>);
+    if (N < 16384) return L(ring_launch<64, 128, 2, 128, 3>);
+    if (N < 65536) return L(ring_launch<128, 128, 2, 64, 4, 8>);
+    return L(ring_launch<128, 256, 2, 64, 3, 8>);
   }
   if (M <= 256) {
     if (N <= 8192) return L(ring_launch<64, 64, 2, 128, 4>);
-    if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4>);
-    return L(ring_launch<256, 128, 4, 64, 3>);
+    if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4, 8>);
+    return L(ring_launch<256, 128, 4, 64, 3, 8>);
   }
-  if (N <= 8192) return L(ring_launch<128, 128, 2, 64, 4>);
-  return L(ring_launch<256, 128, 4, 64, 3>);
+  if (N <= 8192) return L(ring_launch<128, 128, 2, 64, 4, 8>);
+  if (N < 16384) return L(ring_launch<128, 256, 2, 64, 3, 8>);
+  if (N < 65536) return L(ring_launch<256, 128, 4, 64, 3, 8>);
+  return L(ring_launch<256, 128, 8, 64, 3, 8>);
 }
 
 }  // namespace
