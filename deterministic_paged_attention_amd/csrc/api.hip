@@ -580,9 +580,9 @@ bi_status bi_check_page_table(const int32_t* page_table_host, int32_t page_table
 
 bi_status bi_argmax(const float* x_dev, int64_t ld, int64_t rows, int64_t n, int32_t* out_dev, void* stream) {
   if (rows < 0 || n < 1 || ld < n) return fail(BI_ERR_INVALID_ARG, "rows >= 0, n >= 1 and ld >= n required");
-  if (rows > 0x7fffffffLL) return fail(BI_ERR_OUT_OF_RANGE, "too many rows");
+  if (rows > 0x7fffffffLL || n > 0x7fffffffLL) return fail(BI_ERR_OUT_OF_RANGE, "rows and n must fit in int32");
   if (rows == 0) return ok();
-  if (!x_dev || !out_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  if (!x_dev || !out_dev || ((uintptr_t)x_dev & 3)) return fail(BI_ERR_INVALID_ARG, "null or misaligned device pointer");
   return hip_status(bi::launch_argmax(x_dev, ld, rows, n, out_dev, (hipStream_t)stream), "argmax launch");
 }
 

@@ -122,10 +122,13 @@ __global__ __launch_bounds__(256) void gated_gelu_kernel(const uint16_t* in, int
 }
 
 // Greedy sampling: out[row] = the smallest index i with x[row, i] maximal
-// (NaN never wins; an all-NaN row gives 0).  One workgroup per row; each
-// thread scans a strided slice in increasing index, then (value, index) pairs
-// are combined by "larger value, else smaller index" — a total order, so the
-// result is the same whatever the combining tree.
+// (NaN never wins; an all-NaN row gives 0).  One workgroup of 1024 threads per
+// row: each pass issues kArgUnroll independent 16-byte loads per thread before
+// comparing any of them, so a single row keeps enough reads in flight to
+// stream a 256K-entry vocabulary from one compute unit.  (value, index) pairs
+// are combined by "larger value, else smaller index", a total order, so the
+// result does not depend on which thread saw which element or on the
+// combining tree.
 struct ArgBest {
   float v;
   int64_t i;  // -1: nothing seen
@@ -138,15 +141,50 @@ __device__ __forceinline__ ArgBest arg_better(ArgBest a, ArgBest b) {
   return b;
 }
 
-__global__ __launch_bounds__(256) void argmax_kernel(const float* x, int64_t ld, int64_t n, int32_t* out) {
-  __shared__ float sv[4];
-  __shared__ int64_t si[4];
+__device__ __forceinline__ void arg_consider(ArgBest& b, float v, int64_t i) {
+  if (v == v && (b.i < 0 || v > b.v || (v == b.v && i < b.i))) b = ArgBest{v, i};
+}
+
+constexpr int kArgThreads = 1024;
+constexpr int kArgUnroll = 8;
+
+__global__ __launch_bounds__(kArgThreads) void argmax_kernel(const float* x, int64_t ld, int64_t n, int32_t* out) {
+  __shared__ float sv[kArgThreads / 64];
+  __shared__ int64_t si[kArgThreads / 64];
+  const int t = threadIdx.x;
   const float* xr = x + (int64_t)blockIdx.x * ld;
   ArgBest b{0.f, -1};
-  for (int64_t i = threadIdx.x; i < n; i += 256) {
-    const float v = xr[i];
-    if (v == v && (b.i < 0 || v > b.v)) b = ArgBest{v, i};
+  // scalar head up to the first 16-byte boundary (x is 4-byte aligned)
+  int64_t head = (int64_t)(((16 - ((uintptr_t)xr & 15)) & 15) >> 2);
+  if (head > n) head = n;
+  if (t < head) arg_consider(b, xr[t], t);
+  const float4* xv = reinterpret_cast<const float4*>(xr + head);
+  const int64_t nv = (n - head) >> 2;
+  constexpr int64_t kPass = (int64_t)kArgThreads * kArgUnroll;
+  const int64_t full = nv / kPass * kPass;
+  for (int64_t base = 0; base < full; base += kPass) {
+    float4 r[kArgUnroll];
+#pragma unroll
+    for (int u = 0; u < kArgUnroll; ++u) r[u] = xv[base + u * kArgThreads + t];
+#pragma unroll
+    for (int u = 0; u < kArgUnroll; ++u) {
+      const int64_t i = head + 4 * (base + u * kArgThreads + t);
+      arg_consider(b, r[u].x, i);
+      arg_consider(b, r[u].y, i + 1);
+      arg_consider(b, r[u].z, i + 2);
+      arg_consider(b, r[u].w, i + 3);
+    }
   }
+  for (int64_t j = full + t; j < nv; j += kArgThreads) {
+    const float4 r = xv[j];
+    const int64_t i = head + 4 * j;
+    arg_consider(b, r.x, i);
+    arg_consider(b, r.y, i + 1);
+    arg_consider(b, r.z, i + 2);
+    arg_consider(b, r.w, i + 3);
+  }
+  const int64_t tail = head + 4 * nv;  // at most three scalar entries remain
+  if (tail + t < n) arg_consider(b, xr[tail + t], tail + t);
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) {
     ArgBest o;
@@ -154,15 +192,15 @@ __global__ __launch_bounds__(256) void argmax_kernel(const float* x, int64_t ld,
     o.i = __shfl_xor(b.i, off);
     b = arg_better(b, o);
   }
-  const int wave = threadIdx.x >> 6;
-  if ((threadIdx.x & 63) == 0) {
+  const int wave = t >> 6;
+  if ((t & 63) == 0) {
     sv[wave] = b.v;
     si[wave] = b.i;
   }
   __syncthreads();
-  if (threadIdx.x == 0) {
+  if (t == 0) {
     ArgBest r{sv[0], si[0]};
-    for (int w = 1; w < 4; ++w) r = arg_better(r, ArgBest{sv[w], si[w]});
+    for (int w = 1; w < kArgThreads / 64; ++w) r = arg_better(r, ArgBest{sv[w], si[w]});
     out[blockIdx.x] = r.i < 0 ? 0 : (int32_t)r.i;
   }
 }
@@ -201,7 +239,7 @@ hipError_t launch_add(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t
 
 hipError_t launch_argmax(const float* x, int64_t ld, int64_t rows, int64_t n, int32_t* out, hipStream_t stream) {
   if (rows == 0) return hipSuccess;
-  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(256), 0, stream, x, ld, n, out);
+  hipLaunchKernelGGL(argmax_kernel, dim3((unsigned)rows), dim3(kArgThreads), 0, stream, x, ld, n, out);
   return hipGetLastError();
 }
 

@@ -285,6 +285,8 @@ bi_status bi_check_write_plan(const int32_t* slot_mapping_host, int32_t num_toke
 /* Greedy sampling: out[t] = the smallest index i with x[t, i] maximal over  */
 /* the row (NaN entries never win; a row of NaN gives 0).  x fp32 [rows][n]  */
 /* with row stride ld; out int32 [rows].  Deterministic for any row count.   */
+/* x_dev must be 4-byte aligned; rows and n below 2^31 (BI_ERR_OUT_OF_RANGE  */
+/* otherwise).  One 1024-thread workgroup per row.                           */
 /* ------------------------------------------------------------------------ */
 bi_status bi_argmax(const float* x_dev, int64_t ld, int64_t rows, int64_t n, int32_t* out_dev, void* stream);
 

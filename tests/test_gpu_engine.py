@@ -36,6 +36,20 @@ def test_argmax_parity_ties_nan_and_full_vocab():
     assert got[5] == 77
     sub = big[:, :100003]                                   # strided rows, odd length
     assert np.array_equal(bi.bi_argmax(sub).cpu().numpy(), oracle.argmax_ref(sub.cpu().numpy()))
+    # rows starting off a 16-byte boundary (scalar head), short rows, ties across the
+    # head / vector body / scalar tail boundaries
+    for start, n in [(1, 100003), (3, 262141), (2, 1), (1, 2), (3, 5), (1, 8195), (2, 65536 + 7)]:
+        v = big[:12, start:start + n]
+        if n >= 8:
+            v[7, n - 1] = v[7, 0] = v[7].max() + 2.0         # first (head) and last (tail) tie
+        got = bi.bi_argmax(v).cpu().numpy()
+        assert np.array_equal(got, oracle.argmax_ref(v.cpu().numpy())), (start, n)
+        if n >= 8:
+            assert got[7] == 0
+    big[9, :] = float("-inf")
+    big[9, 123456] = float("nan")
+    got = bi.bi_argmax(big[:12]).cpu().numpy()
+    assert got[9] == 0 and np.array_equal(got, oracle.argmax_ref(big[:12].cpu().numpy()))
 
 
 @pytest.fixture(scope="module")
