@@ -284,6 +284,10 @@ bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split,
     return fail(BI_ERR_OUT_OF_RANGE, "too many work items");
   if ((int64_t)c.num_tokens * cfg->desc.num_q_heads * ns > 0x7fffffffffffLL)
     return fail(BI_ERR_OUT_OF_RANGE, "workspace index overflow");
+  // The partials of one query-row block are written with 32-bit byte offsets
+  // from the block's first partial: bound their span.
+  if ((int64_t)16 * cfg->desc.num_q_heads * ns * cfg->desc.head_dim * 4 > 0x7fffffffLL)
+    return fail(BI_ERR_OUT_OF_RANGE, "H_q * ceil(max_seq_len / split) * D too large");
   bi::AttnSplitArgs a;
   a.q = (const uint16_t*)c.q;
   a.q_stride = c.q_row_stride;

@@ -152,6 +152,8 @@ bi_status bi_kv_write(const bi_attn_config* cfg,
 /*   plan: int32  [num_seqs+1] first work item of each sequence (the split   */
 /*         phase's own schedule), at the first 256-byte boundary after acc   */
 /* Only the splits that meet [lo, p] of a row are written and read.          */
+/* BI_ERR_OUT_OF_RANGE when 16 * H_q * NS * D * 4 >= 2^31 (the partials of    */
+/* one 16-column block are addressed with 32-bit offsets).                   */
 /* ------------------------------------------------------------------------ */
 bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                             int32_t max_seq_len, size_t* bytes);
