@@ -485,6 +485,33 @@ __global__ __launch_bounds__(256) void splitk_reduce_kernel(const float* partial
 }  // namespace
 
 namespace {
+// Workgroups of one ring configuration the current device keeps resident at
+// once (all compute units; computed once per device; 0 if unknown).
+template <int BM, int BN, int WM, int BK, int STAGES, int NW = 4>
+int64_t ring_capacity() {
+  static int64_t cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_ring_kernel<BM, BN, WM, BK, STAGES, NW>, 64 * NW, 0) !=
+      hipSuccess)
+    return 0;
+  cached[dev] = (int64_t)cus * per_cu;
+  return cached[dev];
+}
+
+// True when every workgroup of the configuration is resident at once (one
+// round), as in ring_launch's grid.
+template <int BM, int BN, int WM, int BK, int STAGES, int NW = 4>
+bool ring_fits(int64_t M, int64_t N) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  const int64_t groups = (tiles + kXcds - 1) / kXcds * kXcds;
+  const int64_t cap = ring_capacity<BM, BN, WM, BK, STAGES, NW>();
+  return cap == 0 || groups <= cap;
+}
+
 // Tile configuration by (M, N); with nsplit > 1 the K ranges of ksplit_len
 // run as one launch into fp32 partials.  N here is the partial's width.
 hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c, int64_t ldc,
@@ -504,26 +531,42 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
     if (N < 16384) return L(ring_launch<32, 32, 2, 256, 2>);
     return L(ring_launch<64, 64, 2, 128, 2>);
   }
+  // Up to N = 8192 the tiles are small and the run is latency-bound: a
+  // configuration whose workgroups do not all fit on the GPU at once runs a
+  // second, partly empty round, so the deeper ring (one workgroup per CU)
+  // gives way to a shallower one (two per CU) or to larger tiles.
   if (M <= 32) {
-    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 4>);
+    if (N <= 8192) {
+      if (ring_fits<32, 32, 2, 256, 4>(M, N)) return L(ring_launch<32, 32, 2, 256, 4>);
+      return L(ring_launch<32, 32, 2, 256, 2>);
+    }
     if (N < 16384) return L(ring_launch<32, 64, 2, 128, 5>);
     return L(ring_launch<64, 64, 2, 128, 2>);
   }
   if (M <= 64) {
-    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 4>);
+    if (N <= 8192) {
+      if (ring_fits<32, 32, 2, 256, 4>(M, N)) return L(ring_launch<32, 32, 2, 256, 4>);
+      return L(ring_launch<32, 32, 2, 256, 2>);
+    }
     if (N < 16384) return L(ring_launch<64, 64, 2, 128, 4>);
     return L(ring_launch<64, 128, 2, 128, 3>);
   }
   // Above M = 64, eight-wave workgroups (two waves per SIMD) let one wave's
   // LDS reads overlap another's MFMAs.
   if (M <= 128) {
-    if (N <= 8192) return L(ring_launch<32, 32, 2, 256, 2>);
+    if (N <= 8192) {
+      if (ring_fits<32, 32, 2, 256, 2>(M, N)) return L(ring_launch<32, 32, 2, 256, 2>);
+      return L(ring_launch<64, 64, 2, 128, 4>);
+    }
     if (N < 16384) return L(ring_launch<64, 128, 2, 128, 3>);
     if (N < 65536) return L(ring_launch<128, 128, 2, 64, 4, 8>);
     return L(ring_launch<128, 256, 2, 64, 3, 8>);
   }
   if (M <= 256) {
-    if (N <= 8192) return L(ring_launch<64, 64, 2, 128, 4>);
+    if (N <= 8192) {
+      if (ring_fits<64, 64, 2, 128, 4>(M, N)) return L(ring_launch<64, 64, 2, 128, 4>);
+      return L(ring_launch<64, 64, 2, 128, 2>);
+    }
     if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4, 8>);
     return L(ring_launch<256, 128, 4, 64, 3, 8>);
   }
