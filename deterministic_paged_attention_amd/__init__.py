@@ -95,6 +95,7 @@ _sig("bi_embedding", c_i32, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_i64, c_vp)
 _sig("bi_qk_norm_rope", c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
      ctypes.c_double, c_vp)
 _sig("bi_add", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
+_sig("bi_add_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c_vp)
 _sig("bi_gated_gelu", c_i32, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_status_string", ctypes.c_char_p, c_i32)
 _sig("bi_last_error_message", ctypes.c_char_p)
@@ -414,6 +415,29 @@ def bi_add(a, b, out=None, stream=None):
     ld = lambda t: t.stride(0) if R > 1 else N  # noqa: E731
     _check(lib.bi_add(_ptr(a), ld(a), _ptr(b), ld(b), _ptr(out), ld(out), R, N, _stream(stream)))
     return out
+
+
+def bi_add_rmsnorm(a, b, gamma, eps, sum_out=None, out=None, stream=None):
+    """(s, y) with s = a + b and y = rmsnorm(s): one launch, bitwise equal to
+    bi_add followed by bi_rmsnorm.  sum_out may be a or b (in place)."""
+    torch = _torch()
+    _need(a, torch.bfloat16, "a")
+    _need(b, torch.bfloat16, "b")
+    _need(gamma, torch.bfloat16, "gamma")
+    M, H = a.shape
+    if sum_out is None:
+        sum_out = torch.empty((M, H), dtype=torch.bfloat16, device=a.device)
+    if out is None:
+        out = torch.empty((M, H), dtype=torch.bfloat16, device=a.device)
+    for t, nm in ((a, "a"), (b, "b"), (sum_out, "sum_out"), (out, "out")):
+        if t.stride(1) != 1:
+            raise ValueError(f"rows of {nm} must be contiguous")
+    if not gamma.is_contiguous():
+        raise ValueError("gamma must be contiguous")
+    ld = lambda t: t.stride(0) if M > 1 else H  # noqa: E731
+    _check(lib.bi_add_rmsnorm(_ptr(a), ld(a), _ptr(b), ld(b), _ptr(sum_out), ld(sum_out), _ptr(gamma), float(eps), M, H,
+                              _ptr(out), ld(out), _stream(stream)))
+    return sum_out, out
 
 
 def bi_gated_gelu(x, out=None, stream=None):

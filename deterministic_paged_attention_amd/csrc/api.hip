@@ -507,6 +507,27 @@ bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens,
                     "qk_norm_rope launch");
 }
 
+bi_status bi_add_rmsnorm(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* s_dev, int64_t ld_s,
+                         const void* gamma_dev, float eps, int64_t M, int64_t H, void* y_dev, int64_t ld_y,
+                         void* stream) {
+  if (M < 0 || H < 8 || H % 8 != 0)
+    return fail(BI_ERR_INVALID_ARG, "M must be >= 0 and H a positive multiple of 8 (M=%lld H=%lld)", (long long)M,
+                (long long)H);
+  if (lda < H || ldb < H || ld_s < H || ld_y < H || lda % 8 || ldb % 8 || ld_s % 8 || ld_y % 8)
+    return fail(BI_ERR_INVALID_ARG, "row strides must be >= H and multiples of 8");
+  if (!(eps >= 0.f) || std::isinf(eps)) return fail(BI_ERR_INVALID_ARG, "eps must be finite and >= 0");
+  if (M > 0x7fffffffLL) return fail(BI_ERR_OUT_OF_RANGE, "M too large");
+  if (M == 0) return ok();
+  if (!a_dev || !b_dev || !s_dev || !gamma_dev || !y_dev) return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(a_dev, 16) || !aligned(b_dev, 16) || !aligned(s_dev, 16) || !aligned(gamma_dev, 16) ||
+      !aligned(y_dev, 16))
+    return fail(BI_ERR_INVALID_ARG, "a, b, s, gamma and y must be 16-byte aligned");
+  return hip_status(bi::launch_add_rmsnorm((const uint16_t*)a_dev, lda, (const uint16_t*)b_dev, ldb,
+                                           (uint16_t*)s_dev, ld_s, (const uint16_t*)gamma_dev, eps, M, H,
+                                           (uint16_t*)y_dev, ld_y, (hipStream_t)stream),
+                    "add_rmsnorm launch");
+}
+
 bi_status bi_add(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* c_dev, int64_t ldc,
                  int64_t rows, int64_t n, void* stream) {
   if (rows < 0 || n < 0 || lda < n || ldb < n || ldc < n) return fail(BI_ERR_INVALID_ARG, "bad add shape");

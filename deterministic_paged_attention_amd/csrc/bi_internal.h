@@ -71,6 +71,9 @@ hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new
 
 hipError_t launch_rmsnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
                           int64_t M, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);
+hipError_t launch_add_rmsnorm(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, uint16_t* s,
+                              int64_t lds, const uint16_t* gamma, float eps, int64_t M, int64_t H, uint16_t* y,
+                              int64_t ldy, hipStream_t stream);
 
 // out_kind: 0 = bf16, 1 = fp32.  k range [k_begin, k_begin + k_len_per_split) per
 // blockIdx.z when k_splits > 1 (partials to fp32 [k_splits][M][N], ldc = N).

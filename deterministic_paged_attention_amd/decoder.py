@@ -21,7 +21,7 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import (AttnConfig, alloc_workspace, bi_add, bi_embedding, bi_gated_gelu, bi_gemm, bi_kv_write,
+from . import (AttnConfig, alloc_workspace, bi_add, bi_add_rmsnorm, bi_embedding, bi_gated_gelu, bi_gemm, bi_kv_write,
                bi_paged_attention, bi_paged_attention_workspace_size, bi_qk_norm_rope, bi_rmsnorm, bi_slot_mapping)
 
 
@@ -108,13 +108,15 @@ class Decoder:
         h = bi_embedding(self.w["embed"], ids)
         if capture is not None:
             keep("embed.out", h)
+        # Each residual add is fused with the RMSNorm that follows it (the next
+        # block's input norm); the values are those of the separate add and norm.
+        xn = bi_rmsnorm(h, self.w["layers"][0]["g_attn"], s.eps) if nl > 0 else None
         for layer in range(nl):
             W = self.w["layers"][layer]
             c = self.cfg(layer)
             k_cache, v_cache = caches[layer]
             cap = layer in cap_layers
             pre = f"l{layer}."
-            xn = bi_rmsnorm(h, W["g_attn"], s.eps)
             qkv = bi_gemm(xn, W["w_qkv"])
             if cap:
                 keep(pre + "h_in", h); keep(pre + "xn", xn); keep(pre + "qkv_raw", qkv)
@@ -127,12 +129,14 @@ class Decoder:
             attn = bi_paged_attention(c, q, k_cache, v_cache, page_table, seq_lens, query_start_loc, max_seq_len,
                                       workspace=ws)
             o = bi_gemm(attn.view(T, Hq * D), W["w_o"])
-            h2 = bi_add(h, o)
-            xn2 = bi_rmsnorm(h2, W["g_mlp"], s.eps)
+            h2, xn2 = bi_add_rmsnorm(h, o, W["g_mlp"], s.eps)
             gu = bi_gemm(xn2, W["w_gu"])
             act = bi_gated_gelu(gu)
             dn = bi_gemm(act, W["w_down"])
-            h3 = bi_add(h2, dn)
+            if layer + 1 < nl:
+                h3, xn = bi_add_rmsnorm(h2, dn, self.w["layers"][layer + 1]["g_attn"], s.eps)
+            else:
+                h3 = bi_add(h2, dn)
             if cap:
                 keep(pre + "qkv", qkv); keep(pre + "attn", attn); keep(pre + "o", o); keep(pre + "h_mid", h2)
                 keep(pre + "xn2", xn2); keep(pre + "gu", gu); keep(pre + "act", act); keep(pre + "down", dn)

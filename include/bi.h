@@ -251,6 +251,16 @@ bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens,
                           int32_t num_kv_heads, int32_t head_dim, const void* gamma_q_dev,
                           const void* gamma_k_dev, float eps, double rope_theta, void* stream);
 
+/* Residual add fused with the RMSNorm that follows it in a pre-norm block:
+ * s = a + b (as bi_add) and y = rmsnorm(s, gamma, eps) (as bi_rmsnorm on s),
+ * in one launch; s and y are bitwise those of the two calls.  All bf16,
+ * rows of H (a positive multiple of 8) with row strides lda, ldb, ld_s, ld_y
+ * (multiples of 8); pointers 16-byte aligned.  s may alias a or b; y must not
+ * overlap a, b or s. */
+bi_status bi_add_rmsnorm(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* s_dev, int64_t ld_s,
+                         const void* gamma_dev, float eps, int64_t M, int64_t H, void* y_dev, int64_t ld_y,
+                         void* stream);
+
 /* c = a + b elementwise (fp32 add, one bf16 rounding); rows x n with row
  * strides lda, ldb, ldc.  c may alias a or b. */
 bi_status bi_add(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* c_dev, int64_t ldc,

@@ -221,6 +221,34 @@ def test_rmsnorm_ragged_hidden_and_strides():
     assert (out[:, H:].float() == 0).all()
 
 
+@pytest.mark.parametrize("M,H", [(1, 2560), (7, 4096), (256, 2560), (3, 8)])
+def test_add_rmsnorm_is_add_then_rmsnorm(M, H):
+    """The fused residual add + norm equals the two separate launches bit for
+    bit, and both equal the oracle's norm of the bf16-rounded sum."""
+    a = synth.normal_bf16((M, H), 405).to(DEV)
+    b = synth.normal_bf16((M, H), 406, std=3.0).to(DEV)
+    g = synth.normal_bf16((H,), 407, std=0.1, mean=1.0).to(DEV)
+    s_ref = bi.bi_add(a, b)
+    y_ref = bi.bi_rmsnorm(s_ref, g, 1e-6)
+    s, y = bi.bi_add_rmsnorm(a, b, g, 1e-6)
+    assert torch.equal(s.view(torch.int16), s_ref.view(torch.int16))
+    assert torch.equal(y.view(torch.int16), y_ref.view(torch.int16))
+    sum64 = synth.to_f64(a.cpu()) + synth.to_f64(b.cpu())
+    # the fp64 sum of two bf16 values is exact: rounded to fp32, then to bf16
+    assert np.array_equal(synth.to_f64(s.cpu()),
+                          synth.to_f64(torch.from_numpy(sum64).to(torch.float32).to(torch.bfloat16)))
+    ref = oracle.rmsnorm_ref(synth.to_f64(s.cpu()), synth.to_f64(g.cpu()), 1e-6)
+    assert np.max(np.abs(synth.to_f64(y.cpu()) - ref)) <= BF16_TOL
+    # in place on a, with strided rows
+    big = torch.zeros((M, H + 24), dtype=torch.bfloat16, device=DEV)
+    big[:, :H] = a
+    out = torch.zeros((M, H + 8), dtype=torch.bfloat16, device=DEV)
+    bi.bi_add_rmsnorm(big[:, :H], b, g, 1e-6, sum_out=big[:, :H], out=out[:, :H])
+    assert torch.equal(big[:, :H].view(torch.int16), s_ref.view(torch.int16))
+    assert torch.equal(out[:, :H].view(torch.int16), y_ref.view(torch.int16))
+    assert (big[:, H:].float() == 0).all() and (out[:, H:].float() == 0).all()
+
+
 # ---------------------------------------------------------------- a5: GEMM
 
 def test_gemm_small_integers_exact_fp32():
