@@ -94,6 +94,8 @@ _sig("bi_gemm_splitk", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i6
 _sig("bi_embedding", c_i32, c_vp, c_i64, c_i64, c_vp, c_i32, c_vp, c_i64, c_vp)
 _sig("bi_qk_norm_rope", c_i32, c_vp, c_i64, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp, c_f32,
      ctypes.c_double, c_vp)
+_sig("bi_qk_norm_rope_kv_write", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_i32, c_vp, c_vp, c_f32, ctypes.c_double,
+     c_vp, c_vp, c_vp, c_i32, c_vp)
 _sig("bi_add", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_add_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c_vp)
 _sig("bi_gated_gelu", c_i32, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
@@ -402,6 +404,26 @@ def bi_qk_norm_rope(qkv, seq_lens, query_start_loc, num_q_heads, num_kv_heads, h
     _check(lib.bi_qk_norm_rope(_ptr(qkv), rs, T, _ptr(seq_lens), _ptr(query_start_loc), seq_lens.shape[0],
                                num_q_heads, num_kv_heads, head_dim, _ptr(gamma_q), _ptr(gamma_k), float(eps),
                                float(rope_theta), _stream(stream)))
+    return qkv
+
+
+def bi_qk_norm_rope_kv_write(cfg: AttnConfig, qkv, seq_lens, query_start_loc, gamma_q, gamma_k, eps, rope_theta,
+                             slot_mapping, k_cache, v_cache, stream=None):
+    """bi_qk_norm_rope on qkv [T, (H_q + 2 H_kv) D] in place, fused with the cache
+    write of its k and v parts at slot_mapping (one launch)."""
+    torch = _torch()
+    _need(qkv, torch.bfloat16, "qkv")
+    _need(k_cache, torch.bfloat16, "k_cache")
+    _need(v_cache, torch.bfloat16, "v_cache")
+    _need(slot_mapping, torch.int32, "slot_mapping")
+    T = qkv.shape[0]
+    rs = qkv.stride(0) if T > 1 else qkv.shape[1]
+    if qkv.stride(1) != 1 or not (k_cache.is_contiguous() and v_cache.is_contiguous()):
+        raise ValueError("qkv rows and the caches must be contiguous")
+    _check(lib.bi_qk_norm_rope_kv_write(cfg.handle, _ptr(qkv), rs, T, _ptr(seq_lens), _ptr(query_start_loc),
+                                        seq_lens.shape[0], _ptr(gamma_q), _ptr(gamma_k), float(eps), float(rope_theta),
+                                        _ptr(slot_mapping), _ptr(k_cache), _ptr(v_cache), k_cache.shape[0],
+                                        _stream(stream)))
     return qkv
 
 

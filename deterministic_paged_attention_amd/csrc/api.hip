@@ -503,8 +503,33 @@ bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens,
   return hip_status(bi::launch_qk_norm_rope((uint16_t*)qkv_dev, row_stride, num_tokens, seq_lens_dev,
                                             query_start_loc_dev, num_seqs, num_q_heads, num_kv_heads, head_dim,
                                             (const uint16_t*)gamma_q_dev, (const uint16_t*)gamma_k_dev, eps,
-                                            rope_theta, (hipStream_t)stream),
+                                            rope_theta, nullptr, nullptr, nullptr, 0, (hipStream_t)stream),
                     "qk_norm_rope launch");
+}
+
+bi_status bi_qk_norm_rope_kv_write(const bi_attn_config* cfg, void* qkv_dev, int64_t row_stride, int32_t num_tokens,
+                                   const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev, int32_t num_seqs,
+                                   const void* gamma_q_dev, const void* gamma_k_dev, float eps, double rope_theta,
+                                   const int32_t* slot_mapping_dev, void* k_cache_dev, void* v_cache_dev,
+                                   int32_t num_pages, void* stream) {
+  if (bi_status st = check_cfg(cfg)) return st;
+  const bi_attn_desc& d = cfg->desc;
+  if (num_seqs < 1 || num_tokens < 0 || num_pages < 1)
+    return fail(BI_ERR_INVALID_ARG, "num_seqs >= 1, num_tokens >= 0 and num_pages >= 1 required");
+  if (row_stride < (int64_t)(d.num_q_heads + 2 * d.num_kv_heads) * d.head_dim)
+    return fail(BI_ERR_INVALID_ARG, "row_stride smaller than the q, k and v parts of a row");
+  if (!(eps >= 0.f) || std::isinf(eps) || !(rope_theta > 1.0) || std::isinf(rope_theta))
+    return fail(BI_ERR_INVALID_ARG, "eps must be finite and >= 0, rope_theta finite and > 1");
+  if (num_tokens == 0) return ok();
+  if (!qkv_dev || !seq_lens_dev || !query_start_loc_dev || !gamma_q_dev || !gamma_k_dev || !slot_mapping_dev ||
+      !k_cache_dev || !v_cache_dev)
+    return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  return hip_status(bi::launch_qk_norm_rope((uint16_t*)qkv_dev, row_stride, num_tokens, seq_lens_dev,
+                                            query_start_loc_dev, num_seqs, d.num_q_heads, d.num_kv_heads, d.head_dim,
+                                            (const uint16_t*)gamma_q_dev, (const uint16_t*)gamma_k_dev, eps,
+                                            rope_theta, slot_mapping_dev, (uint16_t*)k_cache_dev,
+                                            (uint16_t*)v_cache_dev, num_pages, (hipStream_t)stream),
+                    "qk_norm_rope_kv_write launch");
 }
 
 bi_status bi_add_rmsnorm(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb, void* s_dev, int64_t ld_s,

@@ -88,10 +88,12 @@ hipError_t launch_gemm_splitk_reduce(const float* partial, int32_t k_splits, int
 
 hipError_t launch_embedding(const uint16_t* table, int64_t vocab, int64_t hidden, const int32_t* ids,
                             int32_t num_tokens, uint16_t* out, int64_t ld_out, hipStream_t stream);
+// slots == nullptr: q and k rows only; otherwise also the cache write of k and v.
 hipError_t launch_qk_norm_rope(uint16_t* qkv, int64_t row_stride, int32_t num_tokens, const int32_t* seq_lens,
                                const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, const uint16_t* gamma_q, const uint16_t* gamma_k, float eps,
-                               double theta, hipStream_t stream);
+                               double theta, const int32_t* slots, uint16_t* k_cache, uint16_t* v_cache,
+                               int32_t num_pages, hipStream_t stream);
 hipError_t launch_add(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, uint16_t* c, int64_t ldc,
                       int64_t rows, int64_t n, hipStream_t stream);
 hipError_t launch_argmax(const float* x, int64_t ld, int64_t rows, int64_t n, int32_t* out, hipStream_t stream);

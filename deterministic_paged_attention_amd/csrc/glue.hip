@@ -44,31 +44,18 @@ __global__ __launch_bounds__(256) void embedding_kernel(const uint16_t* table, i
   *reinterpret_cast<u32x4*>(out + t * ld_out + 8 * c) = v;
 }
 
-// One wave per (token, head) row of the q and k parts of a fused QKV row.
+// Normalise and rotate one head row x (head_dim D) in place, one wave:
 //   y = x / sqrt(sum x^2 / D + eps) * gamma         (fp32; fixed tree over D)
 //   z_i       = y_i cos(a_i) - y_{i+D/2} sin(a_i)
 //   z_{i+D/2} = y_i sin(a_i) + y_{i+D/2} cos(a_i),  a_i = p * theta^(-2i/D),  i < D/2
-// with p = k_len - q_len + j the row's logical position.  The angle and its
-// sine and cosine are evaluated in fp64 and rounded once to fp32; the result
-// is rounded once to bf16 and written in place.
-__global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_t row_stride, int32_t num_tokens,
-                                                           const int32_t* seq_lens, const int32_t* qsl,
-                                                           int32_t num_seqs, int32_t num_q_heads,
-                                                           int32_t num_kv_heads, int32_t head_dim,
-                                                           const uint16_t* gamma_q, const uint16_t* gamma_k,
-                                                           float eps, double log2_theta) {
-  const int lane = threadIdx.x & 63;
-  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
-  const int heads = num_q_heads + num_kv_heads;
-  if (row >= (int64_t)num_tokens * heads) return;
-  const int t = (int)(row / heads);
-  const int h = (int)(row % heads);
-  const int s = find_token_seq(qsl, num_seqs, t);
-  const int p = seq_lens[s] - (qsl[s + 1] - qsl[s]) + (t - qsl[s]);
-  uint16_t* x = qkv + (int64_t)t * row_stride + (int64_t)h * head_dim;
-  const uint16_t* g = h < num_q_heads ? gamma_q : gamma_k;
+// with p the row's logical position.  The angle and its sine and cosine are
+// evaluated in fp64 and rounded once to fp32; the result is rounded once to
+// bf16.  This lane owns the pairs (i, i + D/2) for i = lane, lane + 64 (at most
+// two for D <= 256); their results are returned in z[j] (i) and z[2 + j]
+// (i + D/2), as bf16 bits.
+__device__ __forceinline__ void norm_rope_row(uint16_t* x, const uint16_t* g, int head_dim, int p, float eps,
+                                              double log2_theta, int lane, uint16_t (&z)[4]) {
   const int half = head_dim / 2;
-  // This lane owns the pairs (i, i + D/2) for i = lane, lane + 64, ...  (at most 2 for D <= 256).
   float a[2] = {0.f, 0.f}, b[2] = {0.f, 0.f};
   float ss = 0.f;
 #pragma unroll
@@ -87,13 +74,73 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_
 #pragma unroll
   for (int j = 0; j < 2; ++j) {
     const int i = lane + 64 * j;
+    z[j] = z[2 + j] = 0;
     if (i < half) {
       const float ya = (a[j] * inv) * bf16_to_f32(g[i]);
       const float yb = (b[j] * inv) * bf16_to_f32(g[i + half]);
       const double ang = (double)p * exp2(-(double)(2 * i) / (double)head_dim * log2_theta);
       const float c = (float)cos(ang), sn = (float)sin(ang);
-      x[i] = f32_to_bf16(ya * c - yb * sn);
-      x[i + half] = f32_to_bf16(ya * sn + yb * c);
+      z[j] = f32_to_bf16(ya * c - yb * sn);
+      z[2 + j] = f32_to_bf16(ya * sn + yb * c);
+      x[i] = z[j];
+      x[i + half] = z[2 + j];
+    }
+  }
+}
+
+// Element offsets, inside one (page, KV head) block of 16 tokens, of
+// head-dim element d of token slot o, in the cache layouts
+//   K [D/8][16][8]:          ((d / 8) * 16 + o) * 8 + d % 8
+//   V [D/32][16][16][2]:     d = 32 np + 16 e + r  ->  ((np * 16 + r) * 16 + o) * 2 + e
+__device__ __forceinline__ int64_t k_elem(int d, int o) { return ((int64_t)(d >> 3) * 16 + o) * 8 + (d & 7); }
+__device__ __forceinline__ int64_t v_elem(int d, int o) {
+  return ((int64_t)((d >> 5) * 16 + (d & 15)) * 16 + o) * 2 + ((d >> 4) & 1);
+}
+
+// One wave per (token, head) row of the q and k parts of a fused QKV row
+// (norm_rope_row on each, in place).  With slots != nullptr the kernel also
+// covers the v part and writes each token's k (after the rotation) and v rows
+// into the paged caches at slots[t] (skipped for a negative slot or a page
+// past the pool), exactly as the separate cache write does.
+__global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_t row_stride, int32_t num_tokens,
+                                                           const int32_t* seq_lens, const int32_t* qsl,
+                                                           int32_t num_seqs, int32_t num_q_heads,
+                                                           int32_t num_kv_heads, int32_t head_dim,
+                                                           const uint16_t* gamma_q, const uint16_t* gamma_k,
+                                                           float eps, double log2_theta, const int32_t* slots,
+                                                           uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages) {
+  const int lane = threadIdx.x & 63;
+  const int64_t row = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  const int heads = num_q_heads + num_kv_heads * (slots ? 2 : 1);
+  if (row >= (int64_t)num_tokens * heads) return;
+  const int t = (int)(row / heads);
+  const int h = (int)(row % heads);
+  uint16_t* x = qkv + (int64_t)t * row_stride + (int64_t)h * head_dim;
+  int64_t base = -1;  // element offset of this token's (page, KV head) block in the caches
+  if (slots && h >= num_q_heads) {
+    const int slot = slots[t];
+    if (slot >= 0 && (slot >> 4) < num_pages)
+      base = ((int64_t)(slot >> 4) * num_kv_heads + (h - num_q_heads) % num_kv_heads) * ((int64_t)head_dim * 16);
+  }
+  if (h >= num_q_heads + num_kv_heads) {  // v row: copy into the cache
+    if (base < 0) return;
+    const int o = slots[t] & 15;
+    for (int d = lane; d < head_dim; d += 64) v_cache[base + v_elem(d, o)] = x[d];
+    return;
+  }
+  const int s = find_token_seq(qsl, num_seqs, t);
+  const int p = seq_lens[s] - (qsl[s + 1] - qsl[s]) + (t - qsl[s]);
+  uint16_t z[4];
+  norm_rope_row(x, h < num_q_heads ? gamma_q : gamma_k, head_dim, p, eps, log2_theta, lane, z);
+  if (base >= 0) {  // k row: the rotated values into the cache
+    const int o = slots[t] & 15, half = head_dim / 2;
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int i = lane + 64 * j;
+      if (i < half) {
+        k_cache[base + k_elem(i, o)] = z[j];
+        k_cache[base + k_elem(i + half, o)] = z[2 + j];
+      }
     }
   }
 }
@@ -221,12 +268,13 @@ hipError_t launch_embedding(const uint16_t* table, int64_t vocab, int64_t hidden
 hipError_t launch_qk_norm_rope(uint16_t* qkv, int64_t row_stride, int32_t num_tokens, const int32_t* seq_lens,
                                const int32_t* qsl, int32_t num_seqs, int32_t num_q_heads, int32_t num_kv_heads,
                                int32_t head_dim, const uint16_t* gamma_q, const uint16_t* gamma_k, float eps,
-                               double theta, hipStream_t stream) {
-  const int64_t rows = (int64_t)num_tokens * (num_q_heads + num_kv_heads);
+                               double theta, const int32_t* slots, uint16_t* k_cache, uint16_t* v_cache,
+                               int32_t num_pages, hipStream_t stream) {
+  const int64_t rows = (int64_t)num_tokens * (num_q_heads + num_kv_heads * (slots ? 2 : 1));
   if (rows == 0) return hipSuccess;
   hipLaunchKernelGGL(qk_norm_rope_kernel, dim3((unsigned)((rows + 3) / 4)), dim3(256), 0, stream, qkv, row_stride,
                      num_tokens, seq_lens, qsl, num_seqs, num_q_heads, num_kv_heads, head_dim, gamma_q, gamma_k,
-                     eps, log2(theta));
+                     eps, log2(theta), slots, k_cache, v_cache, num_pages);
   return hipGetLastError();
 }
 

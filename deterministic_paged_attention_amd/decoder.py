@@ -21,8 +21,9 @@ from typing import Dict, List, Optional
 
 import torch
 
-from . import (AttnConfig, alloc_workspace, bi_add, bi_add_rmsnorm, bi_embedding, bi_gated_gelu, bi_gemm, bi_kv_write,
-               bi_paged_attention, bi_paged_attention_workspace_size, bi_qk_norm_rope, bi_rmsnorm, bi_slot_mapping)
+from . import (AttnConfig, alloc_workspace, bi_add, bi_add_rmsnorm, bi_embedding, bi_gated_gelu, bi_gemm,
+               bi_paged_attention, bi_paged_attention_workspace_size, bi_qk_norm_rope_kv_write, bi_rmsnorm,
+               bi_slot_mapping)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -121,11 +122,10 @@ class Decoder:
             if cap:
                 keep(pre + "h_in", h); keep(pre + "xn", xn); keep(pre + "qkv_raw", qkv)
             theta = s.theta_global if s.is_global(layer) else s.theta_local
-            bi_qk_norm_rope(qkv, seq_lens, query_start_loc, Hq, Hk, D, W["g_q"], W["g_k"], s.eps, theta)
+            # q/k norm and RoPE in place, fused with the cache write of k and v
+            bi_qk_norm_rope_kv_write(c, qkv, seq_lens, query_start_loc, W["g_q"], W["g_k"], s.eps, theta, slots,
+                                     k_cache, v_cache)
             q = qkv[:, : Hq * D].view(T, Hq, D)
-            k_new = qkv[:, Hq * D: (Hq + Hk) * D].view(T, Hk, D)
-            v_new = qkv[:, (Hq + Hk) * D:].view(T, Hk, D)
-            bi_kv_write(c, k_new, v_new, slots, k_cache, v_cache)
             attn = bi_paged_attention(c, q, k_cache, v_cache, page_table, seq_lens, query_start_loc, max_seq_len,
                                       workspace=ws)
             o = bi_gemm(attn.view(T, Hq * D), W["w_o"])

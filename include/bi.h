@@ -251,6 +251,18 @@ bi_status bi_qk_norm_rope(void* qkv_dev, int64_t row_stride, int32_t num_tokens,
                           int32_t num_kv_heads, int32_t head_dim, const void* gamma_q_dev,
                           const void* gamma_k_dev, float eps, double rope_theta, void* stream);
 
+/* bi_qk_norm_rope on the q and k parts of fused QKV rows [q | k | v] (head
+ * geometry from cfg; row_stride >= (H_q + 2 H_kv) D) fused with the cache
+ * write of bi_kv_write: each token's rotated k heads and its v heads are
+ * stored at slot_mapping[t] in the paged caches (negative slots and pages
+ * past the pool skipped).  The qkv rows and the caches end bitwise as after
+ * bi_qk_norm_rope followed by bi_kv_write of qkv's k and v parts. */
+bi_status bi_qk_norm_rope_kv_write(const bi_attn_config* cfg, void* qkv_dev, int64_t row_stride, int32_t num_tokens,
+                                   const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev, int32_t num_seqs,
+                                   const void* gamma_q_dev, const void* gamma_k_dev, float eps, double rope_theta,
+                                   const int32_t* slot_mapping_dev, void* k_cache_dev, void* v_cache_dev,
+                                   int32_t num_pages, void* stream);
+
 /* Residual add fused with the RMSNorm that follows it in a pre-norm block:
  * s = a + b (as bi_add) and y = rmsnorm(s, gamma, eps) (as bi_rmsnorm on s),
  * in one launch; s and y are bitwise those of the two calls.  All bf16,

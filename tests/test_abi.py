@@ -160,3 +160,24 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.bi_slot_mapping(FAKE, 4, FAKE, FAKE, 0, 3, 16, 10, FAKE, None) == 1
     assert L.bi_paged_attention_merge(cfg.handle, FAKE, FAKE, 2, 2, 64, FAKE, 16, FAKE, None) == 5
     assert L.bi_attn_config_create(None, None) == 1
+
+
+def test_qk_norm_rope_kv_write_rejects_bad_arguments():
+    cfg = bi.AttnConfig(8, 4, 256)
+    L = bi.lib
+    row = (8 + 2 * 4) * 256
+
+    def call(**kw):
+        a = dict(qkv=FAKE, rs=row, nt=3, sl=FAKE, qsl=FAKE, ns=1, gq=FAKE, gk=FAKE, eps=1e-6, theta=1e4, slots=FAKE,
+                 k=FAKE, v=FAKE, np=4)
+        a.update(kw)
+        return L.bi_qk_norm_rope_kv_write(cfg.handle, a["qkv"], a["rs"], a["nt"], a["sl"], a["qsl"], a["ns"], a["gq"],
+                                          a["gk"], a["eps"], a["theta"], a["slots"], a["k"], a["v"], a["np"], None)
+
+    assert call(rs=row - 256) == 1             # the v part must fit in a row
+    assert call(ns=0) == 1
+    assert call(np=0) == 1
+    assert call(eps=-1.0) == 1
+    assert call(theta=1.0) == 1
+    assert call(slots=None) == 1
+    assert call(nt=0) == 0                     # nothing to do

@@ -195,3 +195,33 @@ def test_logits_bitwise_across_batch_chunking_layout_and_prefix_reuse(decoder):
     for r in toks:
         k = (r, prompt[r] - 1)
         assert first_mismatch(alone[k], batched[k]) is None and first_mismatch(alone[k], chunked[k]) is None, k
+
+
+@pytest.mark.parametrize("Hq,Hk,D", [(8, 4, 256), (32, 8, 128), (4, 2, 64)])
+def test_qk_norm_rope_kv_write_is_the_two_launches(Hq, Hk, D):
+    """The fused q/k norm + RoPE + cache write leaves qkv and both caches bitwise
+    as bi_qk_norm_rope followed by bi_kv_write (including a skipped negative slot
+    and rows of sequences at different positions)."""
+    cfg = bi.AttnConfig(Hq, Hk, D)
+    T, num_pages = 11, 9
+    qkv0 = synth.normal_bf16((T, (Hq + 2 * Hk) * D + 8), 610, std=2.0).to(DEV)[:, : (Hq + 2 * Hk) * D]
+    gq = synth.normal_bf16((D,), 611, std=0.1, mean=1.0).to(DEV)
+    gk = synth.normal_bf16((D,), 612, std=0.1, mean=1.0).to(DEV)
+    seq_lens = torch.tensor([40, 7, 300], dtype=torch.int32, device=DEV)
+    qsl = torch.tensor([0, 5, 6, 11], dtype=torch.int32, device=DEV)
+    slots = torch.tensor([3, 17, 18, 19, 140, 70, -1, 5, 127, 128, 2], dtype=torch.int32, device=DEV)
+    caches = []
+    for _ in range(2):
+        k = torch.full(cfg.k_cache_shape(num_pages), float("nan"), dtype=torch.bfloat16, device=DEV)
+        v = torch.full(cfg.v_cache_shape(num_pages), float("nan"), dtype=torch.bfloat16, device=DEV)
+        caches.append((k, v))
+    a = qkv0.clone()
+    bi.bi_qk_norm_rope(a, seq_lens, qsl, Hq, Hk, D, gq, gk, 1e-6, 10000.0)
+    bi.bi_kv_write(cfg, a[:, Hq * D:(Hq + Hk) * D].view(T, Hk, D), a[:, (Hq + Hk) * D:].view(T, Hk, D), slots,
+                   caches[0][0], caches[0][1])
+    b = qkv0.clone()
+    bi.bi_qk_norm_rope_kv_write(cfg, b, seq_lens, qsl, gq, gk, 1e-6, 10000.0, slots, caches[1][0], caches[1][1])
+    assert torch.equal(a.view(torch.int16), b.view(torch.int16))
+    for x, y in zip(caches[0], caches[1]):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+    assert torch.equal(b[:, (Hq + Hk) * D:].view(torch.int16), qkv0[:, (Hq + Hk) * D:].view(torch.int16))
