@@ -36,6 +36,8 @@
 
 #include <math.h>
 
+#include <algorithm>
+
 namespace bi {
 namespace {
 
@@ -518,7 +520,11 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
   w.g4 = lane >> 4;
   w.total = ldc(a.plan, a.num_seqs);
   w.stride = gridDim.x * kSplitWaves;
-  w.u = blockIdx.x * kSplitWaves + wave;
+  // Item u of the first round goes to wave u % kSplitWaves of workgroup
+  // u / kSplitWaves, or, when there are fewer items than waves (spread), to
+  // wave u / gridDim.x of workgroup u % gridDim.x, so that a small batch's
+  // items run on as many compute units as possible.
+  w.u = a.spread ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * kSplitWaves + wave;
   w.cur = decode_item(a, w.u, w.total);
   if (!w.cur.valid) return;
   w.begin_item();
@@ -599,11 +605,24 @@ int resident_split_groups() {
   return cached[dev];
 }
 
+// Upper bound on the work items of a launch, from host-side sizes only:
+// query-row blocks (at most one partial block per sequence) x KV heads x the
+// splits one block can meet (all ns, or with a window the splits of w + 16
+// keys).
+inline int64_t item_bound(const AttnSplitArgs& a, int qb) {
+  const int64_t tq = (int64_t)(kRowsPerBlock >> a.log2_group) * qb;
+  const int64_t blocks = ((int64_t)a.num_tokens + tq - 1) / tq + a.num_seqs;
+  int64_t splits = a.ns;
+  if (a.window > 0) splits = std::min<int64_t>(splits, (a.window + tq + a.split - 2) / a.split + 1);
+  return blocks * a.num_kv_heads * splits;
+}
+
 template <int D, int QB>
 hipError_t split_launch_qb(AttnSplitArgs a, hipStream_t stream) {
   a.qblocks = QB;
   const int groups = resident_split_groups<D, QB>();
   if (groups <= 0) return hipErrorInvalidDevice;
+  a.spread = item_bound(a, QB) < (int64_t)groups * kSplitWaves ? 1 : 0;
   hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;

@@ -37,6 +37,7 @@ struct AttnSplitArgs {
   float* ws_acc;             // [R][ns][D]
   int32_t* plan;             // [num_seqs + 1]: first work item of each sequence, total last
   int32_t qblocks;           // query-row blocks per work item (set by the launcher)
+  int32_t spread;            // 1: consecutive items go to different workgroups (set by the launcher)
 };
 
 struct AttnMergeArgs {
