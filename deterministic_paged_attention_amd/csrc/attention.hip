@@ -200,12 +200,25 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // overlap; every row still goes through exactly the operations, in exactly the
 // order, it would alone.  A row with no visible key in the tile keeps
 // (m, l, acc) bit-for-bit (select, not update).
+//
+// Two wave-uniform shortcuts leave every value bit-for-bit as computed in
+// full: the key masks are applied only when some row of the wave does not see
+// all 32 keys of the tile (a masked score is -inf, an unmasked one passes
+// unchanged), and the accumulators are rescaled only when some row has a new
+// maximum (otherwise alpha is exp2(0) = 1 exactly, or 0 on an accumulator
+// that is still +0, so acc * alpha == acc).  Rescaling in place before the PV
+// product equals scaling its input: a row without a visible key has
+// m_new == m and keeps its accumulator either way.
 template <int D, int QB>
 __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const TileData<D>& t,
                                              const ItemLane<D> (&L)[QB], int tile, int g4, float qk_scale_log2) {
   constexpr int NSTEP = D / 32;
   constexpr int NBLK = D / 16;
   const int kb = tile << 5;
+  bool inside = true;
+#pragma unroll
+  for (int b = 0; b < QB; ++b) inside &= L[b].rm.lo <= kb && kb + 31 <= L[b].rm.hi;
+  const bool any_masked = __builtin_amdgcn_ballot_w64(!inside) != 0;
   // Scores: lane holds keys kb + 16h + 4*g4 + i (i = 0..3) of its row.
   float x[QB][2][4];
 #pragma unroll
@@ -220,11 +233,18 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = kb + 16 * h + 4 * g4 + i;
-        const bool ok = key >= L[b].rm.lo && key <= L[b].rm.hi;
-        x[b][h][i] = ok ? sc[b][i] * qk_scale_log2 : -INFINITY;
-      }
+      for (int i = 0; i < 4; ++i) x[b][h][i] = sc[b][i] * qk_scale_log2;
+  }
+  if (any_masked) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int h = 0; h < 2; ++h)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int key = kb + 16 * h + 4 * g4 + i;
+          if (key < L[b].rm.lo || key > L[b].rm.hi) x[b][h][i] = -INFINITY;
+        }
   }
   float tmax[QB];
 #pragma unroll
@@ -241,11 +261,13 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
   bool live[QB];
   float m_new[QB], alpha[QB], rs[QB];
   bf16x8 pfrag[QB];
+  bool rescale = false;
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     live[b] = tmax[b] != -INFINITY;  // this row sees at least one key here
     m_new[b] = fmaxf(st[b].m, tmax[b]);
     alpha[b] = (st[b].m == -INFINITY) ? 0.f : exp2_hw(st[b].m - m_new[b]);
+    rescale |= st[b].m != -INFINITY && m_new[b] != st[b].m;
     __bf16 pb[2][4];
     rs[b] = 0.f;
 #pragma unroll
@@ -260,6 +282,12 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
   }
 #pragma unroll
   for (int b = 0; b < QB; ++b) rs[b] = row4_sum(rs[b]);
+  if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
+#pragma unroll
+    for (int b = 0; b < QB; ++b)
+#pragma unroll
+      for (int n = 0; n < NBLK; ++n) st[b].acc[n] = st[b].acc[n] * alpha[b];
+  }
 
 #pragma unroll
   for (int n = 0; n < NBLK; ++n) {
@@ -273,8 +301,7 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
                       __builtin_amdgcn_perm(w1.w, w1.z, sel) & t.vmask[1].y};
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
-      const f32x4 cin = st[b].acc[n] * alpha[b];
-      const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag[b], cin);
+      const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag[b], st[b].acc[n]);
       st[b].acc[n] = live[b] ? res : st[b].acc[n];
     }
   }
