@@ -336,15 +336,16 @@ __device__ __forceinline__ SeqSplits seq_splits(int q_len, int k_len, int window
   return r;
 }
 
-__global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) {
-  __shared__ int wave_tot[16];
-  __shared__ int carry_sh;
+// Exclusive prefix sum of the per-sequence item counts over NT threads;
+// store(i, v) receives plan[i] for i < num_seqs and the total at i = num_seqs.
+template <int NT, typename Store>
+__device__ __forceinline__ void plan_scan(const AttnSplitArgs& a, int* wave_tot, int* carry_sh, Store store) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wv = tid >> 6;
   const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;  // query tokens per work item
-  if (tid == 0) carry_sh = 0;
+  if (tid == 0) *carry_sh = 0;
   __syncthreads();
-  for (int base = 0; base < a.num_seqs; base += 1024) {
+  for (int base = 0; base < a.num_seqs; base += NT) {
     const int s = base + tid;
     int c = 0;
     if (s < a.num_seqs) {
@@ -360,15 +361,36 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) 
     }
     if (lane == 63) wave_tot[wv] = incl;
     __syncthreads();
-    int before = carry_sh;
+    int before = *carry_sh;
     for (int w = 0; w < wv; ++w) before += wave_tot[w];
-    if (s < a.num_seqs) a.plan[s] = before + incl - c;
+    if (s < a.num_seqs) store(s, before + incl - c);
     __syncthreads();
-    if (tid == 1023) carry_sh = before + incl;
+    if (tid == NT - 1) *carry_sh = before + incl;
     __syncthreads();
   }
-  if (tid == 0) a.plan[a.num_seqs] = carry_sh;
+  if (tid == 0) store(a.num_seqs, *carry_sh);
 }
+
+__global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) {
+  __shared__ int wave_tot[16];
+  __shared__ int carry_sh;
+  plan_scan<1024>(a, wave_tot, &carry_sh, [&](int i, int v) { a.plan[i] = v; });
+}
+
+// Up to this many sequences, every workgroup of the split kernel computes the
+// plan itself into LDS at its start (the scan costs each workgroup less than
+// the separate launch it replaces); beyond it a one-workgroup launch writes the
+// plan to the workspace first.
+constexpr int kLdsPlanSeqs = 2048;
+
+// Plan entry i, from the workgroup's LDS copy or from the workspace; both are
+// wave-uniform.
+struct PlanView {
+  const int* lds;  // nullptr: the workspace copy a.plan
+  __device__ __forceinline__ int at(const AttnSplitArgs& a, int i) const {
+    return lds ? __builtin_amdgcn_readfirstlane(lds[i]) : ldc(a.plan, i);
+  }
+};
 
 // Wave-uniform description of one item.
 struct Item {
@@ -379,7 +401,7 @@ struct Item {
   const int32_t* pt_row;
 };
 
-__device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, int u, int total) {
+__device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, const PlanView& pv, int u, int total) {
   Item it;
   it.valid = u < total;
   it.s = 0; it.kvh = 0; it.sigma = 0; it.q0 = 0; it.tq0 = 0; it.nrow_tok = 0; it.k_len = 0; it.p_first = 0;
@@ -388,10 +410,10 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, int u, int t
   int lo = 0, hi = a.num_seqs - 1;  // largest s with plan[s] <= u
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
-    if (ldc(a.plan, mid) <= u) lo = mid; else hi = mid - 1;
+    if (pv.at(a, mid) <= u) lo = mid; else hi = mid - 1;
   }
   const int s = lo;
-  const int local = u - ldc(a.plan, s);
+  const int local = u - pv.at(a, s);
   const int q0 = ldc(a.qsl, s);
   const int q_len = ldc(a.qsl, s + 1) - q0;
   const int k_len = ldc(a.seq_lens, s);
@@ -495,6 +517,7 @@ __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item
 template <int D, int QB>
 struct SplitWave {
   const AttnSplitArgs& a;
+  PlanView pv;
   int lane, g4, total, stride, u;
   Item cur, nxt;
   ItemLane<D> curL[QB];
@@ -531,7 +554,7 @@ struct SplitWave {
     begin_item();  // Q loads overlap the tile loads already in flight
     u += stride;
     ct = cur.tile_begin;
-    nxt = decode_item(a, u + stride, total);
+    nxt = decode_item(a, pv, u + stride, total);
     return true;
   }
 };
@@ -542,20 +565,29 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
   // Wave index, made visibly wave-uniform so everything derived from the
   // item index stays in scalar registers (scalar page-table loads).
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  __shared__ int plan_s[kLdsPlanSeqs + 1];
+  __shared__ int wave_tot[kSplitWaves];
+  __shared__ int carry_sh;
   SplitWave<D, QB> w{a};
+  w.pv.lds = nullptr;
+  if (a.num_seqs <= kLdsPlanSeqs) {
+    plan_scan<64 * kSplitWaves>(a, wave_tot, &carry_sh, [&](int i, int v) { plan_s[i] = v; });
+    __syncthreads();
+    w.pv.lds = plan_s;
+  }
   w.lane = lane;
   w.g4 = lane >> 4;
-  w.total = ldc(a.plan, a.num_seqs);
+  w.total = w.pv.at(a, a.num_seqs);
   w.stride = gridDim.x * kSplitWaves;
   // Item u of the first round goes to wave u % kSplitWaves of workgroup
   // u / kSplitWaves, or, when there are fewer items than waves (spread), to
   // wave u / gridDim.x of workgroup u % gridDim.x, so that a small batch's
   // items run on as many compute units as possible.
   w.u = a.spread ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * kSplitWaves + wave;
-  w.cur = decode_item(a, w.u, w.total);
+  w.cur = decode_item(a, w.pv, w.u, w.total);
   if (!w.cur.valid) return;
   w.begin_item();
-  w.nxt = decode_item(a, w.u + w.stride, w.total);
+  w.nxt = decode_item(a, w.pv, w.u + w.stride, w.total);
   w.ct = w.cur.tile_begin;
   TileData<D> buf0, buf1;
   load_tile(a, w.cur.kvh, w.cur.k_len, w.ct, w.cur.tile_end, tile_pages(w.cur.pt_row, w.cur.last_entry, w.ct),
@@ -650,9 +682,11 @@ hipError_t split_launch_qb(AttnSplitArgs a, hipStream_t stream) {
   const int groups = resident_split_groups<D, QB>();
   if (groups <= 0) return hipErrorInvalidDevice;
   a.spread = item_bound(a, QB) < (int64_t)groups * kSplitWaves ? 1 : 0;
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.num_seqs > kLdsPlanSeqs) {
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL((attn_split_kernel<D, QB>), dim3(groups), dim3(64 * kSplitWaves), 0, stream, a);
   return hipGetLastError();
 }
