@@ -86,6 +86,20 @@ def test_decode_batch_composition_order_and_page_layout():
         assert _assert_same(ref, got, name) == 24
 
 
+def test_plan_in_lds_and_in_workspace_agree():
+    """Above 2048 sequences the split phase reads its work plan from the
+    workspace (written by a separate launch); below, each workgroup builds it
+    in LDS.  The same decode rows through both paths are bitwise equal."""
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=32)
+    n = 2100
+    reqs = _pool(geom, n, seed=41, lo=1, hi=90)
+    ids = list(range(n))
+    ref = _decode_last(cfg, reqs, [ids[i:i + 700] for i in range(0, n, 700)], page_seed=3)
+    got = _decode_last(cfg, reqs, [ids[::-1]], page_seed=4)
+    assert _assert_same(ref, got, "plan in workspace vs in LDS") == n
+
+
 def test_decode_mixed_short_and_long_contexts_under_window():
     """Window 1024 with contexts below and above it in one batch (a batch-wide
     K-length bound must not change any row)."""
