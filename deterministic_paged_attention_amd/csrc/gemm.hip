@@ -570,7 +570,12 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
     if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4, 8>);
     return L(ring_launch<256, 128, 4, 64, 3, 8>);
   }
-  if (N <= 8192) return L(ring_launch<128, 128, 2, 64, 4, 8>);
+  if (N <= 8192) {
+    // 128 x 128 tiles while they fit in one round, else 128 x 256 (M = 2048:
+    // 2560 x 10240 220 -> 188 us; 6144 x 4096 at M = 1024 99 -> 82 us)
+    if (ring_fits<128, 128, 2, 64, 4, 8>(M, N)) return L(ring_launch<128, 128, 2, 64, 4, 8>);
+    return L(ring_launch<128, 256, 2, 64, 3, 8>);
+  }
   if (N < 16384) return L(ring_launch<128, 256, 2, 64, 3, 8>);
   if (N < 65536) return L(ring_launch<256, 128, 4, 64, 3, 8>);
   return L(ring_launch<256, 128, 8, 64, 3, 8>);
