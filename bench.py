@@ -137,18 +137,17 @@ def bench_decode(args):
     q = qkv[:, : HQ * D].view(B, HQ, D)
     k_new = qkv[:, HQ * D: (HQ + HKV) * D].view(B, HKV, D)
     v_new = qkv[:, (HQ + HKV) * D:].view(B, HKV, D)
-    slots = torch.empty(B, dtype=torch.int32, device=dev)
     attn = torch.empty((B, HQ, D), dtype=torch.bfloat16, device=dev)
     y = torch.empty((B, HIDDEN), dtype=torch.bfloat16, device=dev)
     ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, B, wl.max_seq_len))
     stream = torch.cuda.current_stream()
 
-    names = ["rmsnorm", "gemm_qkv", "slot_mapping", "kv_write", "attn_split", "attn_merge", "gemm_o"]
+    # slot mapping + KV write as one launch (bi_kv_write_paged: slots from the page table)
+    names = ["rmsnorm", "gemm_qkv", "kv_write", "attn_split", "attn_merge", "gemm_o"]
     launches = [
         lambda: bi.bi_rmsnorm(x, gamma, 1e-5, out=xn),
         lambda: bi.bi_gemm(xn, w_qkv, out=qkv),
-        lambda: bi.bi_slot_mapping(wl.page_table, wl.seq_lens, wl.qsl, B, P, wl.num_pages, out=slots),
-        lambda: bi.bi_kv_write(cfg, k_new, v_new, slots, wl.k_cache, wl.v_cache),
+        lambda: bi.bi_kv_write_paged(cfg, k_new, v_new, wl.page_table, wl.seq_lens, wl.qsl, wl.k_cache, wl.v_cache),
         lambda: bi.bi_paged_attention_split(cfg, q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
                                             wl.max_seq_len, ws),
         lambda: bi.bi_paged_attention_merge(cfg, wl.seq_lens, wl.qsl, B, wl.max_seq_len, ws, out=attn),
@@ -213,8 +212,8 @@ def bench_decode(args):
         out_k = torch.empty_like(attn)
 
         def run_inv():
-            launches[4]()
-            launches[5]()
+            launches[SPLIT]()
+            launches[SPLIT + 1]()
 
         def splitk_runner(n):
             ws_k = bi.alloc_workspace(bi.bi_paged_attention_splitk_workspace_size(cfg, B, B, wl.max_seq_len, n))

@@ -65,6 +65,8 @@ _sig("bi_attn_config_query", c_i32, c_vp, ctypes.POINTER(bi_attn_desc), P_i32)
 _sig("bi_kv_cache_bytes", c_i32, c_vp, c_i64, ctypes.POINTER(c_sz))
 _sig("bi_slot_mapping", c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp)
 _sig("bi_kv_write", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32, c_vp)
+_sig("bi_kv_write_paged", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_vp, c_vp, c_i32,
+     c_vp)
 _sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_item_blocks", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
@@ -214,6 +216,24 @@ def bi_kv_write(cfg: AttnConfig, k_new, v_new, slot_mapping, k_cache, v_cache, s
     _check(lib.bi_kv_write(cfg.handle, _ptr(k_new), _row_stride(k_new, "k_new") if n else cfg.num_kv_heads * cfg.head_dim,
                            _ptr(v_new), _row_stride(v_new, "v_new") if n else cfg.num_kv_heads * cfg.head_dim,
                            _ptr(slot_mapping), n, _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(stream)))
+
+
+def bi_kv_write_paged(cfg: AttnConfig, k_new, v_new, page_table, seq_lens, query_start_loc, k_cache, v_cache,
+                      stream=None):
+    """bi_slot_mapping + bi_kv_write in one launch (slots from the page table)."""
+    torch = _torch()
+    _need(k_new, torch.bfloat16, "k_new")
+    _need(v_new, torch.bfloat16, "v_new")
+    for t, nm in ((page_table, "page_table"), (seq_lens, "seq_lens"), (query_start_loc, "query_start_loc")):
+        _need(t, torch.int32, nm)
+    if not page_table.is_contiguous():
+        raise ValueError("page_table must be contiguous")
+    n = k_new.shape[0]
+    row = cfg.num_kv_heads * cfg.head_dim
+    _check(lib.bi_kv_write_paged(cfg.handle, _ptr(k_new), _row_stride(k_new, "k_new") if n else row,
+                                 _ptr(v_new), _row_stride(v_new, "v_new") if n else row, _ptr(page_table),
+                                 page_table.shape[1], _ptr(seq_lens), _ptr(query_start_loc), seq_lens.shape[0], n,
+                                 _ptr(k_cache), _ptr(v_cache), k_cache.shape[0], _stream(stream)))
 
 
 def bi_paged_attention_workspace_size(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int) -> int:

@@ -227,6 +227,34 @@ bi_status bi_kv_write(const bi_attn_config* cfg, const void* k_new_dev, int64_t 
                     "kv_write launch");
 }
 
+bi_status bi_kv_write_paged(const bi_attn_config* cfg, const void* k_new_dev, int64_t k_row_stride,
+                            const void* v_new_dev, int64_t v_row_stride, const int32_t* page_table_dev,
+                            int32_t page_table_stride, const int32_t* seq_lens_dev,
+                            const int32_t* query_start_loc_dev, int32_t num_seqs, int32_t num_tokens,
+                            void* k_cache_dev, void* v_cache_dev, int32_t num_pages, void* stream) {
+  if (bi_status st = check_cfg(cfg)) return st;
+  const bi_attn_desc& d = cfg->desc;
+  if (num_seqs < 1 || num_tokens < 0 || page_table_stride < 1 || num_pages < 1)
+    return fail(BI_ERR_INVALID_ARG, "num_seqs >= 1, num_tokens >= 0, stride >= 1, num_pages >= 1 required");
+  if ((int64_t)num_pages * d.page_size > 0x7fffffffLL)
+    return fail(BI_ERR_OUT_OF_RANGE, "num_pages * page_size overflows a 32-bit slot index");
+  const int64_t row = (int64_t)d.num_kv_heads * d.head_dim;
+  if (k_row_stride < row || v_row_stride < row || k_row_stride % 8 || v_row_stride % 8)
+    return fail(BI_ERR_INVALID_ARG, "k/v row strides must be >= H_kv*D = %lld and multiples of 8", (long long)row);
+  if (num_tokens == 0) return ok();
+  if (!k_new_dev || !v_new_dev || !page_table_dev || !seq_lens_dev || !query_start_loc_dev || !k_cache_dev ||
+      !v_cache_dev)
+    return fail(BI_ERR_INVALID_ARG, "null device pointer");
+  if (!aligned(k_new_dev, 16) || !aligned(v_new_dev, 16) || !aligned(k_cache_dev, 16) || !aligned(v_cache_dev, 16))
+    return fail(BI_ERR_INVALID_ARG, "k_new, v_new and the caches must be 16-byte aligned");
+  return hip_status(bi::launch_kv_write_paged(d.head_dim, d.num_kv_heads, (const uint16_t*)k_new_dev, k_row_stride,
+                                              (const uint16_t*)v_new_dev, v_row_stride, page_table_dev,
+                                              page_table_stride, seq_lens_dev, query_start_loc_dev, num_seqs,
+                                              num_tokens, (uint16_t*)k_cache_dev, (uint16_t*)v_cache_dev, num_pages,
+                                              (hipStream_t)stream),
+                    "kv_write_paged launch");
+}
+
 bi_status bi_paged_attention_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                             int32_t max_seq_len, size_t* bytes) {
   if (bi_status st = check_cfg(cfg)) return st;

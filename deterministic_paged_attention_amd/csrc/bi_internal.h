@@ -69,6 +69,12 @@ hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new
                            const uint16_t* v_new, int64_t v_stride, const int32_t* slots,
                            int32_t num_tokens, uint16_t* k_cache, uint16_t* v_cache,
                            int32_t num_pages, hipStream_t stream);
+// As launch_kv_write with each token's slot computed from the page table
+// (the slot-mapping kernel's rule, page size 16).
+hipError_t launch_kv_write_paged(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
+                                 const uint16_t* v_new, int64_t v_stride, const int32_t* page_table, int32_t stride,
+                                 const int32_t* seq_lens, const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
+                                 uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream);
 
 hipError_t launch_rmsnorm(const uint16_t* x, int64_t ldx, const uint16_t* gamma, float eps,
                           int64_t M, int64_t H, uint16_t* y, int64_t ldy, hipStream_t stream);

@@ -23,13 +23,12 @@ __device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, 
   return lo;
 }
 
-__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_table, int32_t stride,
-                                                           const int32_t* seq_lens, const int32_t* qsl,
-                                                           int32_t num_seqs, int32_t num_tokens,
-                                                           int32_t page_size, int32_t num_pages,
-                                                           int32_t* slots) {
-  const int t = blockIdx.x * 256 + threadIdx.x;
-  if (t >= num_tokens) return;
+// Slot of new token t: page_table[s][p / P] * P + p % P for the token's
+// sequence s and logical position p = seq_lens[s] - q_len_s + j; -1 when the
+// entry is outside the table row or names no page of the pool.
+__device__ __forceinline__ int token_slot(const int32_t* page_table, int32_t stride, const int32_t* seq_lens,
+                                          const int32_t* qsl, int32_t num_seqs, int32_t page_size,
+                                          int32_t num_pages, int t) {
   const int s = find_token_seq(qsl, num_seqs, t);
   const int q0 = qsl[s];
   const int q_len = qsl[s + 1] - q0;
@@ -42,8 +41,32 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_t
       if (pg >= 0 && pg < num_pages) slot = pg * page_size + p % page_size;
     }
   }
-  slots[t] = slot;
+  return slot;
 }
+
+__global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_table, int32_t stride,
+                                                           const int32_t* seq_lens, const int32_t* qsl,
+                                                           int32_t num_seqs, int32_t num_tokens,
+                                                           int32_t page_size, int32_t num_pages,
+                                                           int32_t* slots) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= num_tokens) return;
+  slots[t] = token_slot(page_table, stride, seq_lens, qsl, num_seqs, page_size, num_pages, t);
+}
+
+// Where the cache write finds each token's slot: a slot mapping, or the page
+// table itself (the slot-mapping kernel's computation, done in place).
+struct SlotSource {
+  const int32_t* slots;       // non-null: slots[t]
+  const int32_t* page_table;  // else token_slot over these
+  int32_t stride;
+  const int32_t* seq_lens;
+  const int32_t* qsl;
+  int32_t num_seqs;
+  __device__ __forceinline__ int at(int t, int num_pages) const {
+    return slots ? slots[t] : token_slot(page_table, stride, seq_lens, qsl, num_seqs, 16, num_pages, t);
+  }
+};
 
 // One thread per (token, KV head, 8-element head-dim chunk c).
 // K cache [page][h][D/8][16][8]: the chunk is one 16-byte store.
@@ -52,7 +75,7 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_t
 template <int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
                                                        const uint16_t* v_new, int64_t v_stride,
-                                                       const int32_t* slots, int32_t num_tokens,
+                                                       const SlotSource slots, int32_t num_tokens,
                                                        uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages) {
   constexpr int NC = D / 8;
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -61,7 +84,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const u
   const int c = (int)(gid % NC);
   const int h = (int)((gid / NC) % num_kv_heads);
   const int t = (int)(gid / ((int64_t)NC * num_kv_heads));
-  const int slot = slots[t];
+  const int slot = slots.at(t, num_pages);
   if (slot < 0) return;
   const int pg = slot >> 4;
   const int o = slot & 15;
@@ -82,7 +105,7 @@ __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const u
 
 template <int D>
 hipError_t kv_write_launch(int num_kv_heads, const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
-                           int64_t v_stride, const int32_t* slots, int32_t num_tokens, uint16_t* k_cache,
+                           int64_t v_stride, const SlotSource& slots, int32_t num_tokens, uint16_t* k_cache,
                            uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
   const int64_t total = (int64_t)num_tokens * num_kv_heads * (D / 8);
   if (total == 0) return hipSuccess;
@@ -106,10 +129,24 @@ hipError_t launch_slot_mapping(const int32_t* page_table, int32_t stride, const 
 hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
                            const uint16_t* v_new, int64_t v_stride, const int32_t* slots, int32_t num_tokens,
                            uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
+  const SlotSource src{slots, nullptr, 0, nullptr, nullptr, 0};
   switch (head_dim) {
-    case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
-    case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
-    case 256: return kv_write_launch<256>(num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 256: return kv_write_launch<256>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+hipError_t launch_kv_write_paged(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
+                                 const uint16_t* v_new, int64_t v_stride, const int32_t* page_table, int32_t stride,
+                                 const int32_t* seq_lens, const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
+                                 uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
+  const SlotSource src{nullptr, page_table, stride, seq_lens, qsl, num_seqs};
+  switch (head_dim) {
+    case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
+    case 256: return kv_write_launch<256>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
     default: return hipErrorInvalidValue;
   }
 }

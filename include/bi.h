@@ -126,6 +126,18 @@ bi_status bi_kv_write(const bi_attn_config* cfg,
                       const int32_t* slot_mapping_dev, int32_t num_tokens,
                       void* k_cache_dev, void* v_cache_dev, int32_t num_pages, void* stream);
 
+/* bi_slot_mapping and bi_kv_write in one launch: each new token's slot is
+ * computed from the page table as bi_slot_mapping does (page size 16; a slot
+ * of -1, i.e. a position outside the table row or an entry naming no page of
+ * the pool, is skipped), then its k and v rows are stored there.  The caches
+ * end bitwise as after the two calls; the same write-isolation precondition
+ * applies (bi_check_write_plan on the slots bi_slot_mapping would give). */
+bi_status bi_kv_write_paged(const bi_attn_config* cfg, const void* k_new_dev, int64_t k_row_stride,
+                            const void* v_new_dev, int64_t v_row_stride, const int32_t* page_table_dev,
+                            int32_t page_table_stride, const int32_t* seq_lens_dev,
+                            const int32_t* query_start_loc_dev, int32_t num_seqs, int32_t num_tokens,
+                            void* k_cache_dev, void* v_cache_dev, int32_t num_pages, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Paged attention: decode and chunked prefill through one kernel.           */
 /*                                                                           */

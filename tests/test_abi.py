@@ -181,3 +181,24 @@ def test_qk_norm_rope_kv_write_rejects_bad_arguments():
     assert call(theta=1.0) == 1
     assert call(slots=None) == 1
     assert call(nt=0) == 0                     # nothing to do
+
+
+def test_kv_write_paged_rejects_bad_arguments():
+    cfg = bi.AttnConfig(32, 8, 128)
+    L = bi.lib
+
+    def call(**kw):
+        a = dict(k=FAKE, ks=1024, v=FAKE, vs=1024, pt=FAKE, pts=4, sl=FAKE, qsl=FAKE, ns=2, nt=3, kc=FAKE, vc=FAKE,
+                 np=10)
+        a.update(kw)
+        return L.bi_kv_write_paged(cfg.handle, a["k"], a["ks"], a["v"], a["vs"], a["pt"], a["pts"], a["sl"],
+                                   a["qsl"], a["ns"], a["nt"], a["kc"], a["vc"], a["np"], None)
+
+    assert call(ks=1000) == 1                 # row stride below H_kv * D
+    assert call(pts=0) == 1
+    assert call(ns=0) == 1
+    assert call(np=0) == 1
+    assert call(np=1 << 28) == 3              # slot index would overflow 32 bits
+    assert call(pt=None) == 1
+    assert call(k=FAKE + 8) == 1              # misaligned
+    assert call(nt=0) == 0                    # nothing to do

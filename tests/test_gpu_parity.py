@@ -54,6 +54,45 @@ def test_slot_mapping_and_kv_write_bit_exact():
     kr, vr = oracle.kv_write_ref(k0, v0, synth.to_f64(kn), synth.to_f64(vn), ref, 16)
     np.testing.assert_array_equal(logical_k(kc), kr)   # NaN == NaN positionally
     np.testing.assert_array_equal(logical_v(vc), vr)
+    # the same write with the slots computed in the write kernel from the page table
+    kc2 = nan_cache(cfg.k_cache_shape(plan.num_pages))
+    vc2 = nan_cache(cfg.v_cache_shape(plan.num_pages))
+    bi.bi_kv_write_paged(cfg, kn.to(DEV), vn.to(DEV), pt, sl, qsl, kc2, vc2)
+    assert torch.equal(kc.view(torch.int16), kc2.view(torch.int16))
+    assert torch.equal(vc.view(torch.int16), vc2.view(torch.int16))
+
+
+@pytest.mark.parametrize("Hq,Hk,D", [(32, 8, 128), (8, 4, 256)])
+def test_kv_write_paged_is_slot_mapping_then_kv_write(Hq, Hk, D):
+    """Out-of-pool and negative entries (skipped tokens), ragged q_len, strided k/v rows."""
+    cfg = bi.AttnConfig(Hq, Hk, D)
+    lengths, q_lens = [40, 7, 300, 16], [3, 7, 1, 16]
+    num_pages = 30
+    pt_host = np.full((4, 20), -1, dtype=np.int32)
+    pt_host[0, :3] = [4, 29, 31]          # 31 is past the pool: its tokens are skipped
+    pt_host[1, :1] = [0]
+    pt_host[2, :19] = np.arange(5, 24)
+    pt_host[3, :1] = [-7]                 # negative entry: skipped
+    pt = torch.tensor(pt_host, device=DEV)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    qsl_h = np.concatenate([[0], np.cumsum(q_lens)])
+    qsl = torch.tensor(qsl_h, dtype=torch.int32, device=DEV)
+    T = int(qsl_h[-1])
+    rows = synth.normal_bf16((T, 2 * Hk * D + 16), 620).to(DEV)
+    kn = rows[:, : Hk * D].view(T, Hk, D)
+    vn = rows[:, Hk * D + 16:].view(T, Hk, D)
+    outs = []
+    for paged in (False, True):
+        kc = nan_cache(cfg.k_cache_shape(num_pages))
+        vc = nan_cache(cfg.v_cache_shape(num_pages))
+        if paged:
+            bi.bi_kv_write_paged(cfg, kn, vn, pt, sl, qsl, kc, vc)
+        else:
+            slots = bi.bi_slot_mapping(pt, sl, qsl, T, 16, num_pages)
+            bi.bi_kv_write(cfg, kn, vn, slots, kc, vc)
+        outs.append((kc, vc))
+    for a, b in zip(outs[0], outs[1]):
+        assert torch.equal(a.view(torch.int16), b.view(torch.int16))
 
 
 def test_slot_mapping_out_of_range_pages_give_minus_one():
