@@ -597,6 +597,204 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
 }
 
 // ---------------------------------------------------------------------------
+// Split phase for prefill-shaped batches: workgroup-shared K/V tiles.  A work
+// item holds kSharedBlocks query-row blocks of one (sequence, KV head, split);
+// each of the four waves owns two of them.  The K/V tiles of the item stream
+// through an R-slot LDS ring (buffer loads straight to LDS, 1 KiB per
+// instruction, every wave copying a quarter of each tile), and every wave
+// reads each tile from LDS into exactly the registers load_tile fills and
+// runs the same compute_tile on its two blocks: the arithmetic of every row is
+// the one-block arithmetic, so every bit of its partials is the same.  One
+// copy of a tile feeds eight blocks, and the per-wave state (two blocks, one
+// tile) leaves room for two waves per SIMD.
+//
+// Per step i (all four waves walk the same stream of tiles):
+//   issue this wave's chunks of tile i + R - 1 into slot (i - 1) % R, wait
+//   for this wave's chunks of tile i;  barrier A;  read slot i % R into
+//   registers;  barrier B;  compute tile i for the wave's two blocks (and
+//   write their partials at an item's last tile).
+// Slot (i - 1) % R was read by every wave before barrier B of step i - 1.
+// Each wave issues the same number of copies every step (tiles past the end
+// of the stream copy nothing, through an empty resource), so its wait count
+// is fixed; loads and stores it issues besides only make that wait stronger.
+// ---------------------------------------------------------------------------
+constexpr int kSharedWaves = 4;
+constexpr int kSharedBlocks = 8;  // query-row blocks per item: two per wave
+
+template <int D>
+struct SharedShape {
+  static constexpr int KCH = D / 32;       // 1 KiB chunks per K (or V) page of one KV head
+  static constexpr int NCH = 4 * KCH;      // chunks per tile: K page 0, K page 1, V page 0, V page 1
+  static constexpr int TILE = NCH * 1024;  // bytes per ring slot
+  static constexpr int R = 3;              // ring slots
+  static constexpr int CPW = NCH / kSharedWaves;  // chunks per wave per tile
+  static_assert(NCH % kSharedWaves == 0, "chunks split evenly over the waves");
+};
+
+typedef __attribute__((address_space(3))) void lds_void_t;
+
+template <int n>
+__device__ __forceinline__ void shared_wait_vm() {
+  static_assert(n >= 0 && n < 64, "vmcnt range");
+  // gfx9 encoding: vmcnt[3:0], expcnt[6:4], lgkmcnt[11:8], vmcnt[5:4] in bits [15:14]
+  __builtin_amdgcn_s_waitcnt((n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) << 14));
+}
+
+__device__ __forceinline__ u32x4 shared_lds_read(uint32_t addr) {
+  u32x4 v;
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("ds_read_b128 %0, %1" : "=v"(v) : "v"(addr));
+#else
+  v = u32x4{addr, 0u, 0u, 0u};
+#endif
+  return v;
+}
+
+// Cursor over one workgroup's tile stream: items u, u + G, ... and their tiles.
+struct TileCursor {
+  Item it;
+  int u, t;
+  __device__ __forceinline__ void start(const AttnSplitArgs& a, const PlanView& pv, int u0, int total) {
+    u = u0;
+    it = decode_item(a, pv, u, total);
+    t = it.tile_begin;
+  }
+  // Moves to the next tile; true when that ended the item.
+  __device__ __forceinline__ bool advance(const AttnSplitArgs& a, const PlanView& pv, int stride, int total) {
+    if (++t < it.tile_end) return false;
+    u += stride;
+    it = decode_item(a, pv, u, total);
+    t = it.tile_begin;
+    return true;
+  }
+};
+
+// This wave's chunks (w, w + 4, ...) of the cursor's tile into ring slot `slot`,
+// through the page resources load_tile would use.
+template <int D>
+__device__ __forceinline__ void shared_issue(const AttnSplitArgs& a, const TileCursor& lc, char* ring, int slot,
+                                             int w, int lane) {
+  using S = SharedShape<D>;
+  constexpr int PAGE_BYTES = D * 16 * 2;
+  const int64_t head_elems = (int64_t)D * 16;
+  const int2 pid = tile_pages(lc.it.pt_row, lc.it.last_entry, lc.t);
+  __amdgpu_buffer_rsrc_t rs[4];  // K page 0, K page 1, V page 0, V page 1
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int entry = 2 * lc.t + b;
+    const int raw = b == 0 ? pid.x : pid.y;
+    const int pgc = min(max(raw, 0), a.num_pages - 1);
+    const bool ok = lc.it.valid && lc.t < lc.it.tile_end && entry * 16 < lc.it.k_len && entry < a.pt_stride &&
+                    raw == pgc;
+    const int64_t base = ((int64_t)pgc * a.num_kv_heads + lc.it.kvh) * head_elems;
+    rs[b] = page_rsrc(a.k_cache + base, ok ? PAGE_BYTES : 0);
+    rs[2 + b] = page_rsrc(a.v_cache + base, ok ? PAGE_BYTES : 0);
+  }
+#pragma unroll
+  for (int k = 0; k < S::CPW; ++k) {
+    const int j = w + kSharedWaves * k;  // chunk of the tile
+    lds_void_t* dst = (lds_void_t*)(ring + slot * S::TILE + j * 1024);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j / S::KCH], dst, 16, (j % S::KCH) * 1024 + lane * 16, 0, 0,
+                                             kStreamLoad);
+  }
+}
+
+// The tile in the ring slot at slot_addr into the registers load_tile fills,
+// plus the V zero-fill masks load_tile records.
+template <int D>
+__device__ __forceinline__ void shared_read_tile(const AttnSplitArgs& a, const TileCursor& cc, uint32_t slot_addr,
+                                                 int lane, TileData<D>& t) {
+  using S = SharedShape<D>;
+  const int r = lane & 15, g4 = lane >> 4;
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+#pragma unroll
+    for (int st = 0; st < S::KCH; ++st)
+      t.kf[b][st] = shared_lds_read(slot_addr + (b * S::KCH + st) * 1024 + lane * 16);
+#pragma unroll
+    for (int np = 0; np < S::KCH; ++np)
+      t.vf[b][np] = shared_lds_read(slot_addr + ((2 + b) * S::KCH + np) * 1024 + r * 64 + g4 * 16);
+  }
+#if defined(__HIP_DEVICE_COMPILE__)
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+#pragma unroll
+  for (int b = 0; b < 2; ++b)
+#pragma unroll
+    for (int k = 0; k < S::KCH; ++k) {
+      asm volatile("" : "+v"(t.kf[b][k]));
+      asm volatile("" : "+v"(t.vf[b][k]));
+    }
+#endif
+  const int2 pid = tile_pages(cc.it.pt_row, cc.it.last_entry, cc.t);
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    const int entry = 2 * cc.t + b;
+    const int raw = b == 0 ? pid.x : pid.y;
+    const int pgc = min(max(raw, 0), a.num_pages - 1);
+    const bool ok = entry * 16 < cc.it.k_len && entry < a.pt_stride && raw == pgc;
+    const int nl = min(16, cc.it.k_len - (cc.t * 32 + 16 * b)) - 4 * g4;  // valid keys among this lane's four
+    t.vmask[b].x = !ok ? 0u : (nl >= 2 ? 0xffffffffu : (nl == 1 ? 0x0000ffffu : 0u));
+    t.vmask[b].y = !ok ? 0u : (nl >= 4 ? 0xffffffffu : (nl == 3 ? 0x0000ffffu : 0u));
+  }
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel(const AttnSplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  using S = SharedShape<D>;
+  __shared__ __attribute__((aligned(1024))) char ring[S::R * S::TILE];
+  const int lane = threadIdx.x & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  // The plan comes from the workspace (scalar loads): an LDS copy would be read
+  // by ordinary LDS loads, which the compiler must order after every copy to
+  // LDS still in flight.
+  PlanView pv;
+  pv.lds = nullptr;
+  const int total = pv.at(a, a.num_seqs);
+  const int G = (int)gridDim.x;
+  TileCursor cc, lc;
+  cc.start(a, pv, (int)blockIdx.x, total);
+  if (!cc.it.valid) return;  // the whole workgroup: the item index depends on blockIdx only
+  lc = cc;
+  const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void_t*)ring;
+  for (int p = 0; p < S::R - 1; ++p) {  // tiles 0 .. R - 2 into slots 0 .. R - 2
+    shared_issue<D>(a, lc, ring, p, wave, lane);
+    lc.advance(a, pv, G, total);
+  }
+  SplitState<D> st[2];
+  ItemLane<D> L[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    L[b] = item_lane<D>(a, cc.it, lane, 2 * wave + b);
+    st[b].init();
+  }
+  TileData<D> td;
+  int slot = 0;  // ring slot of step i (i % R)
+  for (;;) {
+    shared_issue<D>(a, lc, ring, slot == 0 ? S::R - 1 : slot - 1, wave, lane);
+    shared_wait_vm<(S::R - 1) * S::CPW>();  // the chunks of the R - 1 later tiles may still fly
+    lc.advance(a, pv, G, total);
+    __builtin_amdgcn_s_barrier();  // A: tile i is in slot `slot`
+    shared_read_tile<D>(a, cc, ring_addr + slot * S::TILE, lane, td);
+    __builtin_amdgcn_s_barrier();  // B: every wave has read slot `slot`
+    compute_tile<D, 2>(st, td, L, cc.t, lane >> 4, a.qk_scale_log2);
+    const Item done = cc.it;
+    if (cc.advance(a, pv, G, total)) {
+#pragma unroll
+      for (int b = 0; b < 2; ++b) {
+        write_partial(a, done, L[b], st[b], lane, 2 * wave + b);
+        L[b] = item_lane<D>(a, cc.it, lane, 2 * wave + b);
+        st[b].init();
+      }
+      if (!cc.it.valid) break;
+    }
+    slot = slot + 1 == S::R ? 0 : slot + 1;
+  }
+  shared_wait_vm<0>();  // no copy outlives the workgroup's LDS
+#endif
+}
+
+// ---------------------------------------------------------------------------
 // Merge phase: one thread per (row, 4 head-dim elements).  Splits are combined
 // in increasing order: m* = max m_s, w_s = 2^(m_s - m*), L = sum w_s l_s,
 // N = sum w_s acc_s, o = N / L.  With a single split w = 1 exactly and the
@@ -700,10 +898,32 @@ hipError_t split_launch_qb(AttnSplitArgs a, hipStream_t stream) {
 // block wide.
 constexpr int kWideBlocks = 4;
 
+// Workgroups of the shared-tile kernel resident at once (per device, cached).
+template <int D>
+int resident_shared_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_split_shared_kernel<D>, 64 * kSharedWaves, 0) !=
+      hipSuccess)
+    return 0;
+  cached[dev] = max(1, cus * max(per_cu, 1));
+  return cached[dev];
+}
+
 template <int D>
 int item_blocks(const AttnSplitArgs& a) {
   if constexpr (D <= 128) {
     const int64_t tq = kRowsPerBlock >> a.log2_group;
+    // shared tiles: on average a full item per sequence and an item per resident workgroup
+    const int64_t shared_items = ((int64_t)a.num_tokens + kSharedBlocks * tq - 1) / (kSharedBlocks * tq) *
+                                 a.num_kv_heads * a.ns;
+    if ((int64_t)a.num_tokens >= kSharedBlocks * tq * (int64_t)a.num_seqs &&
+        shared_items >= (int64_t)resident_shared_groups<D>())
+      return kSharedBlocks;
     const int64_t wide_items = ((int64_t)a.num_tokens + kWideBlocks * tq - 1) / (kWideBlocks * tq) *
                                a.num_kv_heads * a.ns;
     const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
@@ -714,9 +934,24 @@ int item_blocks(const AttnSplitArgs& a) {
 }
 
 template <int D>
+hipError_t shared_launch(AttnSplitArgs a, hipStream_t stream) {
+  a.qblocks = kSharedBlocks;
+  a.spread = 0;
+  const int groups = resident_shared_groups<D>();
+  if (groups <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(attn_split_shared_kernel<D>, dim3(groups), dim3(64 * kSharedWaves), 0, stream, a);
+  return hipGetLastError();
+}
+
+template <int D>
 hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
   if constexpr (D <= 128) {
-    if (item_blocks<D>(a) == kWideBlocks) return split_launch_qb<D, kWideBlocks>(a, stream);
+    const int qb = item_blocks<D>(a);
+    if (qb == kSharedBlocks) return shared_launch<D>(a, stream);
+    if (qb == kWideBlocks) return split_launch_qb<D, kWideBlocks>(a, stream);
   }
   return split_launch_qb<D, 1>(a, stream);
 }

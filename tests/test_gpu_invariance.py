@@ -138,9 +138,9 @@ def test_prefill_chunks_and_token_by_token_agree(geom, window):
     lens = [700, 1300] if window == 0 else [1300, 600]
     reqs = {i: Request(500 + i + window, L, geom) for i, L in enumerate(lens)}
     if geom is LLAMA:
-        # the one-shot prefill runs wide work items, token by token runs one-block items:
-        # the comparison below is then also a cross-mapping check
-        assert bi.bi_paged_attention_item_blocks(cfg, 2, sum(lens), max(lens)) == 4
+        # the one-shot prefill runs workgroup-shared tiles (eight blocks per item), token by
+        # token runs one-block items: the comparison below is then also a cross-mapping check
+        assert bi.bi_paged_attention_item_blocks(cfg, 2, sum(lens), max(lens)) == 8
         assert bi.bi_paged_attention_item_blocks(cfg, 2, 2, max(lens)) == 1
     one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=3)
     assert len(one_shot) == sum(lens)
@@ -149,6 +149,24 @@ def test_prefill_chunks_and_token_by_token_agree(geom, window):
         got = _run_schedule(cfg, reqs, sched, page_seed=pseed, stride_extra=budget % 3)
         n = _assert_same(one_shot, got, f"budget {budget} offset {offset}")
         assert n == sum(lens)
+
+
+def test_wide_and_shared_items_agree_with_one_block_items():
+    """48 requests prefilled in 24-token chunks (about six query blocks per sequence:
+    four-block wide items), in one shot (eight-block shared-tile items) and token by
+    token (one-block items): every row bitwise equal."""
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    reqs = _pool(LLAMA, 48, seed=61, lo=520, hi=700)
+    T24 = 24 * 48
+    assert bi.bi_paged_attention_item_blocks(cfg, 48, T24, 700) == 4
+    T = sum(r.length for r in reqs.values())
+    assert bi.bi_paged_attention_item_blocks(cfg, 48, T, 700) == 8
+    one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=8)
+    chunked = _run_schedule(cfg, reqs, _chunked(reqs, 24), page_seed=9)
+    assert _assert_same(one_shot, chunked, "24-token chunks vs one shot") == T
+    sample = {i: reqs[i] for i in (0, 17, 47)}
+    by_token = _run_schedule(cfg, sample, _chunked(sample, 1), page_seed=10)
+    assert _assert_same(one_shot, by_token, "token by token vs one shot") == sum(r.length for r in sample.values())
 
 
 def test_continuous_batching_mixed_prefill_and_decode_steps():
