@@ -169,6 +169,20 @@ def test_wide_and_shared_items_agree_with_one_block_items():
     assert _assert_same(one_shot, by_token, "token by token vs one shot") == sum(r.length for r in sample.values())
 
 
+def test_shared_items_head_dim_64_agree_with_one_block_items():
+    """Head dim 64 (GQA group 2): one-shot prefill on the shared-tile kernel against the same
+    rows token by token, bitwise."""
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=256)
+    reqs = _pool(geom, 16, seed=71, lo=560, hi=640)
+    T = sum(r.length for r in reqs.values())
+    assert bi.bi_paged_attention_item_blocks(cfg, 16, T, 640) == 8
+    one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=11)
+    sample = {i: reqs[i] for i in (0, 9, 15)}
+    by_token = _run_schedule(cfg, sample, _chunked(sample, 1), page_seed=12)
+    assert _assert_same(one_shot, by_token, "token by token vs one shot") == sum(r.length for r in sample.values())
+
+
 def test_continuous_batching_mixed_prefill_and_decode_steps():
     """One request decodes token by token while others prefill in chunks in the
     same steps; compare with each request run alone in one shot."""
