@@ -191,52 +191,82 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, i
 #pragma unroll
     for (int j = 0; j < MB; ++j) acc[i][j] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+  // Fragments of one group of GK K steps, all read from one stage.
+  auto read_group = [&](uint32_t sa, int kg, u32x4 (&fw)[GK * NB], u32x4 (&fa)[GK * MB]) {
+    const uint32_t sw = sa + BM * BK * 2;
+#pragma unroll
+    for (int q = 0; q < GK; ++q) {
+      const uint32_t cs = (uint32_t)(((4 * (kg + q) + g4) ^ (r & 7)) * 16);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        fw[q * NB + i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
+#pragma unroll
+      for (int j = 0; j < MB; ++j)
+        fa[q * MB + j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
+    }
+  };
+  auto mfma_group = [&](const u32x4 (&fw)[GK * NB], const u32x4 (&fa)[GK * MB]) {
+#pragma unroll
+    for (int q = 0; q < GK; ++q)
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+#pragma unroll
+        for (int j = 0; j < MB; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[q * NB + i]),
+                                                             __builtin_bit_cast(bf16x8, fa[q * MB + j]),
+                                                             acc[i][j], 0, 0, 0);
+  };
+
+  // Software pipeline over groups of K steps: the fragments of group g + 1
+  // are read while the MFMAs of group g run, and waited for (in full) before
+  // the next group; the last group of a slice is carried into the next
+  // iteration, whose first reads (after the barrier) overlap it.  The carried
+  // fragments start as zeros: their MFMAs add exact zeros to the zero
+  // accumulators (+0 + +0 = +0), which changes no bit.  Every element still sees one MFMA per
+  // K step, in increasing K.  The wait closes each group inside the iteration,
+  // so every copy the compiler makes of these registers (the loop-carried
+  // ones included) happens after their data has landed.
+  u32x4 cw[GK * NB], ca[GK * MB];
+#pragma unroll
+  for (int i = 0; i < GK * NB; ++i) cw[i] = u32x4{0u, 0u, 0u, 0u};
+#pragma unroll
+  for (int j = 0; j < GK * MB; ++j) ca[j] = u32x4{0u, 0u, 0u, 0u};
+
+  bool carried = true;                       // wave-uniform
+
 #pragma unroll
   for (int p = 0; p < STAGES - 1; ++p) issue(p);
   for (int64_t s = 0; s < nslices; ++s) {
     // The copies land in LDS behind the compiler's back, so the fragment
     // reads below are explicit ds_read instructions and the waits are ours:
     // this wave's copies of slice s are done (vmcnt), then everyone's are and
-    // nobody still reads slice s-1 (barrier).
+    // nobody still reads slice s-1 (barrier; the carried group is already in
+    // registers).
     if (G % NW == 0 || wave < G % NW) wait_vmcnt<IPW * (STAGES - 2)>();
     else wait_vmcnt<(IPW - 1) * (STAGES - 2)>();
     __builtin_amdgcn_s_barrier();
     issue(s + STAGES - 1);                   // into the stage slice s-1 used
     const uint32_t sa = lds_base + (uint32_t)((s % STAGES) * STAGE * 2);
-    const uint32_t sw = sa + BM * BK * 2;
     const int ksteps = (int)min<int64_t>(SPS, nsteps - SPS * s);  // fewer only on a ragged final slice
-    // Full slices: K steps in groups of GK; the fragments of a group are read
-    // together and waited for in full before its MFMAs, which run in step
-    // order (one LDS round trip per group, straight-line code).  A ragged final
-    // slice goes one step at a time.  The reads are not prefetched a group
-    // ahead: the compiler does not know these registers fill asynchronously
-    // and may copy them before the wait.
     if (ksteps == SPS) {
 #pragma unroll
       for (int kg = 0; kg < SPS; kg += GK) {
         u32x4 fw[GK * NB], fa[GK * MB];
-#pragma unroll
-        for (int q = 0; q < GK; ++q) {
-          const uint32_t cs = (uint32_t)(((4 * (kg + q) + g4) ^ (r & 7)) * 16);
-#pragma unroll
-          for (int i = 0; i < NB; ++i)
-            fw[q * NB + i] = lds_read16(sw + (uint32_t)((wn * (BN / WN) + 16 * i + r) * BK * 2) + cs);
-#pragma unroll
-          for (int j = 0; j < MB; ++j)
-            fa[q * MB + j] = lds_read16(sa + (uint32_t)((wm * (BM / WM) + 16 * j + r) * BK * 2) + cs);
-        }
+        read_group(sa, kg, fw, fa);
+        __builtin_amdgcn_sched_barrier(0);   // all reads issued before the MFMAs they overlap,
+        mfma_group(cw, ca);
+        __builtin_amdgcn_sched_barrier(0);   // and waited for only after those MFMAs
         lds_wait<0>(fw, fa);
 #pragma unroll
-        for (int q = 0; q < GK; ++q)
+        for (int i = 0; i < GK * NB; ++i) cw[i] = fw[i];
 #pragma unroll
-          for (int i = 0; i < NB; ++i)
-#pragma unroll
-            for (int j = 0; j < MB; ++j)
-              acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[q * NB + i]),
-                                                                 __builtin_bit_cast(bf16x8, fa[q * MB + j]),
-                                                                 acc[i][j], 0, 0, 0);
+        for (int j = 0; j < GK * MB; ++j) ca[j] = fa[j];
       }
     } else {
+      // Ragged final slice: finish the carried group, then one step at a time.
+      mfma_group(cw, ca);
+      carried = false;
+      const uint32_t sw = sa + BM * BK * 2;
       for (int ks = 0; ks < ksteps; ++ks) {
         const uint32_t cs = (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16);
         u32x4 fw[NB], fa[MB];
@@ -256,6 +286,7 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, i
       }
     }
   }
+  if (carried) mfma_group(cw, ca);           // the last group (none after a ragged slice)
   wait_vmcnt<0>();                           // drain the trailing (empty) copies
 
   // Lane holds C^T[n + 4*g4 + i][m + r] of each block.
