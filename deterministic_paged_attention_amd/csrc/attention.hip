@@ -317,8 +317,10 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
 // Work list.  An item is one (sequence, query-row block, KV head, split).  The
 // plan kernel writes, for every sequence, the index of its first item
 // (an exclusive prefix sum of integer counts, so exact whatever the order);
-// item u of sequence s has local index l = u - first[s], with the split
-// fastest: split = lo_split(s) + l % nsplit(s), then KV head, then row block.
+// item u of sequence s has local index l = u - first[s], with the KV head
+// fastest (kvh = l % H_kv), then the split (lo_split(s) + (l / H_kv) %
+// nsplit(s)), then the row block: neighbouring waves read the heads of the
+// same physical pages together.
 // A row block whose rows see no key of a split still owns that item; it is
 // processed as one fully masked tile and writes nothing.
 // ---------------------------------------------------------------------------
@@ -419,13 +421,14 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, const PlanVi
   const int k_len = ldc(a.seq_lens, s);
   const SeqSplits sp = seq_splits(q_len, k_len, a.window, a.split);
   const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
-  const int sigma = sp.lo + local % sp.n;
-  const int rest = local / sp.n;
+  const int kvh = local % a.num_kv_heads;
+  const int rest = local / a.num_kv_heads;
+  const int sigma = sp.lo + rest % sp.n;
   it.s = s;
-  it.kvh = rest % a.num_kv_heads;
+  it.kvh = kvh;
   it.sigma = sigma;
   it.q0 = q0;
-  it.tq0 = (rest / a.num_kv_heads) * tq;
+  it.tq0 = (rest / sp.n) * tq;
   it.nrow_tok = min(tq, q_len - it.tq0);
   it.k_len = k_len;
   it.p_first = k_len - q_len + it.tq0;
