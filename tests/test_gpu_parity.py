@@ -290,9 +290,16 @@ def test_add_rmsnorm_is_add_then_rmsnorm(M, H):
 
 # ---------------------------------------------------------------- a5: GEMM
 
-def test_gemm_small_integers_exact_fp32():
-    a = synth.small_int_bf16((37, 4096), 501)
-    w = synth.small_int_bf16((300, 4096), 502)
+@pytest.mark.parametrize("M,N,K", [(37, 300, 4096), (16, 300, 4128), (64, 20000, 2080), (200, 5000, 96),
+                                   (129, 12000, 2080), (100, 70000, 1056), (300, 9000, 4128),
+                                   (1024, 16400, 1056)])
+def test_gemm_small_integers_exact_fp32(M, N, K):
+    """Integer inputs make every correct fp32-accumulating product exact, so any
+    lost, repeated or misplaced K step shows.  The shapes reach the skinny kernel
+    and each ring-tile bracket of M and N, with K both a multiple of every slice
+    width and ragged (a partly filled last slice, or a single short one)."""
+    a = synth.small_int_bf16((M, K), 501)
+    w = synth.small_int_bf16((N, K), 502)
     c = bi.bi_gemm(a.to(DEV), w.to(DEV), out_dtype=torch.float32).cpu()
     ref = oracle.gemm_ref(synth.to_f64(a), synth.to_f64(w))
     assert np.array_equal(c.double().numpy(), ref)
