@@ -69,6 +69,32 @@ def measured_traffic(batch: int):
     return t.get("hbm_bytes_per_launch")
 
 
+def measured_stream_read(stream, nbytes=4 << 30, reps=10):
+    """Bandwidth of the library's plain streaming-read reference kernel over one
+    contiguous 4 GiB buffer (about the split kernel's 4.5 GB), timed with HIP
+    events on the stream it runs on; median of `reps` launches: the same GPU's
+    practical read ceiling, quoted beside the published 8 TB/s."""
+    import torch
+    import deterministic_paged_attention_amd as bi
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    sink = torch.empty(bi.lib.bi_bench_stream_read_sink_words(), dtype=torch.int32, device="cuda")
+    for _ in range(3):
+        bi.bi_bench_stream_read(src, sink, stream)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        bi.bi_bench_stream_read(src, sink, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    ts.sort()
+    del src
+    torch.cuda.empty_cache()
+    t = ts[len(ts) // 2]
+    return {"gbps": round(nbytes / t / 1e9, 1), "bytes": nbytes, "us": round(t * 1e6, 1)}
+
+
 def split_bytes(lengths):
     """Algorithmic bytes of one split-phase launch: K+V of every visible key,
     Q, and the page-table entries read."""
@@ -243,6 +269,8 @@ def bench_decode(args):
                   "heuristic_num_splits": heur, "splitk_us_by_num_splits": {str(n): round(v, 2) for n, v in per_n.items()},
                   "overhead": round(t_inv / per_n[best] - 1.0, 4)}
 
+    read_ref = measured_stream_read(stream)
+
     # The oracle runs after the GPU timing: its BLAS threads keep spinning for a
     # while after each call and would delay the host launching the timed steps.
     cpu = None
@@ -277,7 +305,9 @@ def bench_decode(args):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(B),
                      "kernel": "attn_split_kernel<128, 1>", "algorithmic_bytes_per_launch": sb,
-                     "avg_launch_us": round(split_us, 2)},
+                     "avg_launch_us": round(split_us, 2),
+                     "measured_stream_read_gbps": read_ref["gbps"],
+                     "frac_of_measured_stream_read": round(achieved / read_ref["gbps"], 4)},
         "cpu_baseline": cpu,
         "attention_gbps": round(attn_gbps, 2),
         "attention_frac_of_peak": round(attn_gbps / PEAK_HBM_GBPS, 4),

@@ -89,6 +89,8 @@ _sig("bi_prefix_cache_stats", c_i32, c_vp, c_vp)
 _sig("bi_splitk_attention_heuristic", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, P_i32)
 _sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_splitk", c_i32, *_ATTN_ARGS, c_i32, c_vp, c_sz, c_vp, c_vp)
+_sig("bi_bench_stream_read_sink_words", c_i32)
+_sig("bi_bench_stream_read", c_i32, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_gemm_splitk_heuristic", c_i32, c_i64)
 _sig("bi_gemm_splitk_workspace_size", c_i32, c_i64, c_i64, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_gemm_splitk", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_i32, c_vp, c_sz,
@@ -399,6 +401,20 @@ def bi_gemm_splitk(a, w, k_splits, out_dtype=None, out=None, workspace=None, str
     _check(lib.bi_gemm_splitk(*args, k_splits, _ptr(workspace), workspace.numel() * workspace.element_size(),
                               _stream(stream)))
     return out
+
+
+def bi_bench_stream_read(src, sink=None, stream=None):
+    """Streaming-read reference (measurement only): reads every byte of the
+    contiguous device tensor src once; returns the uint32 sink (one xor word
+    per workgroup; their xor is the xor of src's 32-bit words)."""
+    torch = _torch()
+    if not src.is_contiguous():
+        raise ValueError("src must be contiguous")
+    nbytes = src.numel() * src.element_size()
+    if sink is None:
+        sink = torch.empty(lib.bi_bench_stream_read_sink_words(), dtype=torch.int32, device=src.device)
+    _check(lib.bi_bench_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
+    return sink
 
 
 def bi_embedding(table, ids, out=None, stream=None):

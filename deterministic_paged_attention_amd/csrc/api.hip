@@ -629,6 +629,18 @@ bi_status bi_gemm_splitk(const void* a_dev, int64_t lda, const void* w_dev, int6
                     "gemm split-K reduce launch");
 }
 
+int32_t bi_bench_stream_read_sink_words(void) { return bi::kStreamReadGroups; }
+
+bi_status bi_bench_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, void* stream) {
+  if (!sink_dev || !aligned(sink_dev, 4)) return fail(BI_ERR_INVALID_ARG, "sink NULL or not 4-byte aligned");
+  if (bytes % 16 != 0) return fail(BI_ERR_INVALID_ARG, "bytes %zu not a multiple of 16", bytes);
+  if (bytes > 0 && (!src_dev || !aligned(src_dev, 16)))
+    return fail(BI_ERR_INVALID_ARG, "src NULL or not 16-byte aligned");
+  if (bytes > (size_t)0x7fffffffffffffffULL) return fail(BI_ERR_OUT_OF_RANGE, "bytes too large");
+  return hip_status(bi::launch_stream_read(src_dev, (int64_t)bytes, sink_dev, (hipStream_t)stream),
+                    "stream read launch");
+}
+
 bi_status bi_check_page_table(const int32_t* page_table_host, int32_t page_table_stride, const int32_t* seq_lens_host,
                               const int32_t* query_start_loc_host, int32_t num_seqs, int32_t page_size,
                               int32_t num_pages) {

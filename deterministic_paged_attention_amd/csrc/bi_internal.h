@@ -104,6 +104,10 @@ hipError_t launch_qk_norm_rope(uint16_t* qkv, int64_t row_stride, int32_t num_to
 hipError_t launch_add(const uint16_t* a, int64_t lda, const uint16_t* b, int64_t ldb, uint16_t* c, int64_t ldc,
                       int64_t rows, int64_t n, hipStream_t stream);
 hipError_t launch_argmax(const float* x, int64_t ld, int64_t rows, int64_t n, int32_t* out, hipStream_t stream);
+// Streaming-read reference (measurement only): kStreamReadGroups workgroups,
+// sink[g] = xor of the 32-bit words workgroup g read.  bytes % 16 == 0.
+constexpr int kStreamReadGroups = 8192;
+hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
 hipError_t launch_gated_gelu(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int64_t rows,
                              int64_t F, hipStream_t stream);
 

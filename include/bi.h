@@ -421,6 +421,23 @@ bi_status bi_gemm_splitk(const void* a_dev, int64_t lda, const void* w_dev, int6
                          void* workspace_dev, size_t workspace_bytes, void* stream);
 
 /* ------------------------------------------------------------------------ */
+/* Streaming-read reference, for measurement only: the bandwidth a plain     */
+/* read of one contiguous buffer reaches on this GPU, quoted beside the      */
+/* published HBM peak for the bandwidth-bound split phase (the pages report  */
+/* decode as memory-bound; BASELINE's metric is HBM GB/s against peak).      */
+/* ------------------------------------------------------------------------ */
+
+/* Number of uint32 words bi_bench_stream_read writes to its sink. */
+int32_t bi_bench_stream_read_sink_words(void);
+/* Reads every byte of src_dev[0 .. bytes) once (non-temporal 16-byte loads)
+ * and writes to sink_dev[g], g < bi_bench_stream_read_sink_words(), the xor
+ * of the 32-bit words workgroup g read, so the xor of all sink words is the
+ * xor of every 32-bit word of the buffer.  src_dev: device memory, 16-byte
+ * aligned, bytes a multiple of 16 (BI_ERR_INVALID_ARG otherwise; bytes == 0
+ * still writes the sink, all zeros).  Caller owns both buffers. */
+bi_status bi_bench_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, void* stream);
+
+/* ------------------------------------------------------------------------ */
 /* Diagnostics.                                                              */
 /* ------------------------------------------------------------------------ */
 const char* bi_status_string(bi_status status);

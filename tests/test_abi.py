@@ -202,3 +202,14 @@ def test_kv_write_paged_rejects_bad_arguments():
     assert call(pt=None) == 1
     assert call(k=FAKE + 8) == 1              # misaligned
     assert call(nt=0) == 0                    # nothing to do
+
+
+def test_stream_read_rejects_bad_arguments_before_any_launch():
+    """The streaming-read reference validates on the host: a size that is not
+    a multiple of 16, a misaligned or NULL source, or a NULL sink launch nothing."""
+    assert bi.lib.bi_bench_stream_read_sink_words() == 8192
+    sink = ctypes.c_void_p(4096)          # never dereferenced on these paths
+    assert bi.lib.bi_bench_stream_read(ctypes.c_void_p(4096), 24, sink, None) == 1
+    assert bi.lib.bi_bench_stream_read(ctypes.c_void_p(4104), 32, sink, None) == 1
+    assert bi.lib.bi_bench_stream_read(None, 32, sink, None) == 1
+    assert bi.lib.bi_bench_stream_read(ctypes.c_void_p(4096), 32, None, None) == 1

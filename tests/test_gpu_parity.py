@@ -370,3 +370,21 @@ def test_gemm_lm_head_full_size_sampled():
     ref = oracle.gemm_ref(ah, wh)
     got = c[rows][:, cols].cpu().double().numpy()
     assert np.all(np.abs(got - ref) <= 1e-3 * oracle.gemm_abs_ref(ah, wh))
+
+
+@pytest.mark.parametrize("nbytes", [0, 16, 4096 * 16 + 48, (64 << 20) + 1040])
+def test_stream_read_reads_every_byte(nbytes):
+    """The streaming-read reference (measurement only) must read the whole
+    buffer: the xor of its sink equals the xor of the buffer's 32-bit words,
+    and a one-word change anywhere (first, middle, last chunk) changes it."""
+    words = nbytes // 4
+    src = torch.randint(-2**31, 2**31 - 1, (words,), dtype=torch.int32, generator=torch.Generator().manual_seed(9))
+    expect = int(np.bitwise_xor.reduce(src.numpy().view(np.uint32))) if words else 0
+    d = src.to(DEV)
+    got = int(np.bitwise_xor.reduce(bi.bi_bench_stream_read(d).cpu().numpy().view(np.uint32)))
+    assert got == expect
+    for pos in sorted({0, words // 2, words - 1}) if words else []:
+        d2 = d.clone()
+        d2[pos] ^= 0x5A5A5A5A
+        flipped = int(np.bitwise_xor.reduce(bi.bi_bench_stream_read(d2).cpu().numpy().view(np.uint32)))
+        assert flipped == expect ^ 0x5A5A5A5A
