@@ -239,10 +239,10 @@ def test_full_size_llama_decode_sampled_parity():
 
 # ---------------------------------------------------------------- a4: RMSNorm
 
-@pytest.mark.parametrize("M", [1, 7, 64])
-def test_rmsnorm_parity(M):
-    x = synth.normal_bf16((M, 4096), 401)
-    g = synth.normal_bf16((4096,), 402, std=0.1, mean=1.0)
+@pytest.mark.parametrize("M,H", [(1, 4096), (7, 4096), (64, 4096), (3, 12288)])
+def test_rmsnorm_parity(M, H):
+    x = synth.normal_bf16((M, H), 401)
+    g = synth.normal_bf16((H,), 402, std=0.1, mean=1.0)
     y = bi.bi_rmsnorm(x.to(DEV), g.to(DEV), 1e-5).cpu()
     ref = oracle.rmsnorm_ref(synth.to_f64(x), synth.to_f64(g), 1e-5)
     assert np.max(np.abs(synth.to_f64(y) - ref)) <= BF16_TOL
@@ -260,7 +260,7 @@ def test_rmsnorm_ragged_hidden_and_strides():
     assert (out[:, H:].float() == 0).all()
 
 
-@pytest.mark.parametrize("M,H", [(1, 2560), (7, 4096), (256, 2560), (3, 8)])
+@pytest.mark.parametrize("M,H", [(1, 2560), (7, 4096), (256, 2560), (3, 8), (5, 8200), (2, 16384)])
 def test_add_rmsnorm_is_add_then_rmsnorm(M, H):
     """The fused residual add + norm equals the two separate launches bit for
     bit, and both equal the oracle's norm of the bf16-rounded sum."""
