@@ -135,9 +135,28 @@ def cpu_baseline(wl, sample_seqs: int):
         dt += time.perf_counter() - t0
         lens.append(L)
     nbytes = split_bytes(lens) + sample_seqs * HQ * D * 2
-    return {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
-            "sample": f"float64 numpy attention oracle over {sample_seqs} of the {wl.batch} decode sequences of the "
-                      f"same workload (same bytes-per-sequence accounting as the GPU), {dt:.1f} s of oracle time"}
+    out = {"value": round(nbytes / dt / 1e9, 4), "unit": "GB/s", "cores": threads, "kind": "oracle",
+           "sample": f"float64 numpy attention oracle over {sample_seqs} of the {wl.batch} decode sequences of the "
+                     f"same workload (same bytes-per-sequence accounting as the GPU), {dt:.1f} s of oracle time",
+           "affinity_cores": len(os.sched_getaffinity(0))}
+    # The same oracle on one BLAS thread, over the first few sequences.
+    try:
+        from threadpoolctl import threadpool_limits
+        n1 = min(64, sample_seqs)
+        dt1, lens1 = 0.0, []
+        with threadpool_limits(limits=1, user_api="blas"):
+            for s in range(n1):
+                kk, vv, table, L = wl.host_sequence(s)
+                q = synth.to_f64(wl.q[s:s + 1].cpu())
+                t0 = time.perf_counter()
+                oracle.attention_ref(q, kk, vv, table, [L], [0, 1], HKV, P)
+                dt1 += time.perf_counter() - t0
+                lens1.append(L)
+        out["single_core"] = {"value": round((split_bytes(lens1) + n1 * HQ * D * 2) / dt1 / 1e9, 4), "unit": "GB/s",
+                              "cores": 1, "sample": f"the first {n1} sequences, {dt1:.1f} s of oracle time"}
+    except ImportError:  # pragma: no cover
+        pass
+    return out
 
 
 def bench_decode(args):
