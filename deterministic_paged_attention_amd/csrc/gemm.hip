@@ -595,6 +595,10 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
   }
   if (M <= 256) {
     if (N <= 8192) {
+      // Two-wave 32 x 80 tiles while they all fit in one round: N = 2560 makes
+      // 256 of them at M = 256 (Gemma-shaped down projection 2560 x 10240:
+      // 62 -> 50 us; 2560 x 2048: 18 -> 15 us); with a second round they lose.
+      if (ring_fits<32, 80, 2, 128, 4, 2>(M, N)) return L(ring_launch<32, 80, 2, 128, 4, 2>);
       if (ring_fits<64, 64, 2, 128, 4>(M, N)) return L(ring_launch<64, 64, 2, 128, 4>);
       return L(ring_launch<64, 64, 2, 128, 2>);
     }

@@ -291,7 +291,7 @@ def test_add_rmsnorm_is_add_then_rmsnorm(M, H):
 # ---------------------------------------------------------------- a5: GEMM
 
 @pytest.mark.parametrize("M,N,K", [(37, 300, 4096), (16, 300, 4128), (64, 20000, 2080), (200, 5000, 96),
-                                   (129, 12000, 2080), (100, 70000, 1056), (200, 20480, 2080),
+                                   (129, 12000, 2080), (100, 70000, 1056), (200, 20480, 2080), (240, 2560, 2080),
                                    (300, 9000, 4128), (400, 16400, 1056), (1024, 16400, 1056)])
 def test_gemm_small_integers_exact_fp32(M, N, K):
     """Integer inputs make every correct fp32-accumulating product exact, so any
