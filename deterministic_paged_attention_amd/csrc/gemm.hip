@@ -334,7 +334,6 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, i
 // past M are not loaded: they only feed output columns that are discarded.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyBK = 512;
-constexpr int kSkinnyStages = 8;
 
 template <int STAGES>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
