@@ -95,6 +95,31 @@ def measured_stream_read(stream, nbytes=4 << 30, reps=10):
     return {"gbps": round(nbytes / t / 1e9, 1), "bytes": nbytes, "us": round(t * 1e6, 1)}
 
 
+def measured_mfma_peak(rounds=4096, reps=10):
+    """Rate of the library's MFMA throughput reference (the GEMM's own bf16
+    16x16x32 instruction, eight independent accumulators per wave, a full grid),
+    timed with HIP events on the current stream; median of `reps` launches of
+    about 1.1 TFLOP each: the matrix-core rate this GPU sustains, quoted beside
+    the published dense peak."""
+    import torch
+    import deterministic_paged_attention_amd as bi
+    stream = torch.cuda.current_stream()
+    sink, flops = bi.bi_bench_mfma_peak(rounds, 0.0, stream=stream)
+    for _ in range(2):
+        bi.bi_bench_mfma_peak(rounds, 0.0, sink, stream)
+    ts = []
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        bi.bi_bench_mfma_peak(rounds, 0.0, sink, stream)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ts.append(a.elapsed_time(b) * 1e-3)
+    ts.sort()
+    t = ts[len(ts) // 2]
+    return {"tflops": round(flops / t / 1e12, 1), "flops_per_launch": flops, "us": round(t * 1e6, 1)}
+
+
 def split_bytes(lengths):
     """Algorithmic bytes of one split-phase launch: K+V of every visible key,
     Q, and the page-table entries read."""
@@ -505,6 +530,9 @@ def bench_gemm(args):
             w_host = W.cpu()          # the oracle runs after all GPU timing (its BLAS threads spin on)
         del W
         torch.cuda.empty_cache()
+    mfma_ref = measured_mfma_peak()
+    for r in rows:
+        r["mfma_frac_of_measured_peak"] = round(r["gemm_tflops"] / mfma_ref["tflops"], 4)
     if not args.no_cpu_baseline:
         cpu = gemm_cpu_baseline(w_host, args.seed)
     head = [r for r in rows if r["N"] == 14336 and r["M"] == 256][0]
@@ -515,7 +543,7 @@ def bench_gemm(args):
         "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
         "config": {"workload": "rmsnorm + gemm, K 4096, M {1,7,64,256,1024} x N {14336 bf16, 128256 fp32}, "
                                "MALL flushed per rep", "value_row": "N 14336, M 256"},
-        "rows": rows, "cpu_baseline": cpu}), flush=True)
+        "measured_mfma_peak": mfma_ref, "rows": rows, "cpu_baseline": cpu}), flush=True)
 
 
 def gemm_cpu_baseline(W, seed):

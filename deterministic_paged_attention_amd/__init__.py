@@ -89,6 +89,8 @@ _sig("bi_prefix_cache_stats", c_i32, c_vp, c_vp)
 _sig("bi_splitk_attention_heuristic", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, P_i32)
 _sig("bi_paged_attention_splitk_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_splitk", c_i32, *_ATTN_ARGS, c_i32, c_vp, c_sz, c_vp, c_vp)
+_sig("bi_bench_mfma_peak_sink_words", c_i32)
+_sig("bi_bench_mfma_peak", c_i32, c_f32, c_i32, c_vp, ctypes.POINTER(c_i64), c_vp)
 _sig("bi_bench_stream_read_sink_words", c_i32)
 _sig("bi_bench_stream_read", c_i32, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_gemm_splitk_heuristic", c_i32, c_i64)
@@ -415,6 +417,18 @@ def bi_bench_stream_read(src, sink=None, stream=None):
         sink = torch.empty(lib.bi_bench_stream_read_sink_words(), dtype=torch.int32, device=src.device)
     _check(lib.bi_bench_stream_read(_ptr(src), nbytes, _ptr(sink), _stream(stream)))
     return sink
+
+
+def bi_bench_mfma_peak(rounds, value=0.0, sink=None, stream=None):
+    """MFMA throughput reference (measurement only): one launch of `rounds`
+    rounds of eight bf16 MFMAs per wave over a full grid.  Returns (sink,
+    flops) — the per-wave float sink and the launch's flop count."""
+    torch = _torch()
+    if sink is None:
+        sink = torch.empty(lib.bi_bench_mfma_peak_sink_words(), dtype=torch.float32, device="cuda")
+    flops = c_i64()
+    _check(lib.bi_bench_mfma_peak(float(value), int(rounds), _ptr(sink), ctypes.byref(flops), _stream(stream)))
+    return sink, flops.value
 
 
 def bi_embedding(table, ids, out=None, stream=None):

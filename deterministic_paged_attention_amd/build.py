@@ -20,7 +20,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(PKG, "_build")
 LIB = os.path.join(PKG, "libbi.so")
-SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip", "glue.hip", "stream_read.hip",
+SOURCES = ["api.hip", "attention.hip", "kvcache.hip", "rmsnorm.hip", "gemm.hip", "glue.hip", "stream_read.hip", "mfma_peak.hip",
            "prefix_cache.cpp"]
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")

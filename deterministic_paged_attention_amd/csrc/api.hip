@@ -629,6 +629,16 @@ bi_status bi_gemm_splitk(const void* a_dev, int64_t lda, const void* w_dev, int6
                     "gemm split-K reduce launch");
 }
 
+int32_t bi_bench_mfma_peak_sink_words(void) { return bi::kMfmaPeakGroups * 4; }
+
+bi_status bi_bench_mfma_peak(float value, int32_t rounds, float* sink_dev, int64_t* flops, void* stream) {
+  if (!sink_dev || !aligned(sink_dev, 4)) return fail(BI_ERR_INVALID_ARG, "sink NULL or not 4-byte aligned");
+  if (!flops) return fail(BI_ERR_INVALID_ARG, "flops NULL");
+  if (rounds < 4 || rounds % 4 != 0) return fail(BI_ERR_INVALID_ARG, "rounds %d not a positive multiple of 4", rounds);
+  *flops = bi::mfma_peak_flops(rounds);
+  return hip_status(bi::launch_mfma_peak(value, rounds, sink_dev, (hipStream_t)stream), "mfma peak launch");
+}
+
 int32_t bi_bench_stream_read_sink_words(void) { return bi::kStreamReadGroups; }
 
 bi_status bi_bench_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, void* stream) {

@@ -108,6 +108,13 @@ hipError_t launch_argmax(const float* x, int64_t ld, int64_t rows, int64_t n, in
 // sink[g] = xor of the 32-bit words workgroup g read.  bytes % 16 == 0.
 constexpr int kStreamReadGroups = 8192;
 hipError_t launch_stream_read(const void* src, int64_t bytes, uint32_t* sink, hipStream_t stream);
+// MFMA throughput reference (measurement only): kMfmaPeakGroups workgroups of
+// four waves; `rounds` (a multiple of 4) rounds of eight bf16 16x16x32 MFMAs
+// per wave, fragments filled with `value`; sink[wave] = sum of element 0 of
+// the wave's eight accumulators.
+constexpr int kMfmaPeakGroups = 2048;
+hipError_t launch_mfma_peak(float value, int32_t rounds, float* sink, hipStream_t stream);
+int64_t mfma_peak_flops(int32_t rounds);
 hipError_t launch_gated_gelu(const uint16_t* in, int64_t ld_in, uint16_t* out, int64_t ld_out, int64_t rows,
                              int64_t F, hipStream_t stream);
 

@@ -437,6 +437,19 @@ int32_t bi_bench_stream_read_sink_words(void);
  * still writes the sink, all zeros).  Caller owns both buffers. */
 bi_status bi_bench_stream_read(const void* src_dev, size_t bytes, uint32_t* sink_dev, void* stream);
 
+/* MFMA throughput reference, for measurement only: the bf16 rate the       */
+/* matrix cores sustain on this GPU with the GEMM's own instruction          */
+/* (v_mfma_f32_16x16x32_bf16), quoted beside the published dense peak.       */
+/* Launches a fixed grid whose every wave runs `rounds` rounds of eight      */
+/* independent MFMAs on fragments filled with bf16(value) and writes, per    */
+/* wave, the sum of element 0 of its eight accumulators to sink_dev (float,  */
+/* bi_bench_mfma_peak_sink_words() entries; with value 1 and rounds r each   */
+/* entry is 8 * 32 * r when that is exact in fp32).  rounds: a positive      */
+/* multiple of 4 (BI_ERR_INVALID_ARG otherwise).  *flops receives the        */
+/* launch's floating-point operation count (2 per multiply-add).            */
+int32_t bi_bench_mfma_peak_sink_words(void);
+bi_status bi_bench_mfma_peak(float value, int32_t rounds, float* sink_dev, int64_t* flops, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Diagnostics.                                                              */
 /* ------------------------------------------------------------------------ */

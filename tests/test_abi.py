@@ -213,3 +213,13 @@ def test_stream_read_rejects_bad_arguments_before_any_launch():
     assert bi.lib.bi_bench_stream_read(ctypes.c_void_p(4104), 32, sink, None) == 1
     assert bi.lib.bi_bench_stream_read(None, 32, sink, None) == 1
     assert bi.lib.bi_bench_stream_read(ctypes.c_void_p(4096), 32, None, None) == 1
+
+
+def test_mfma_peak_rejects_bad_arguments_before_any_launch():
+    flops = ctypes.c_int64(0)
+    sink = ctypes.c_void_p(4096)          # never dereferenced on these paths
+    assert bi.lib.bi_bench_mfma_peak_sink_words() == 8192
+    for rounds in (0, 3, -4, 6):
+        assert bi.lib.bi_bench_mfma_peak(1.0, rounds, sink, ctypes.byref(flops), None) == 1
+    assert bi.lib.bi_bench_mfma_peak(1.0, 8, None, ctypes.byref(flops), None) == 1
+    assert bi.lib.bi_bench_mfma_peak(1.0, 8, sink, None, None) == 1

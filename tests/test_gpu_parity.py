@@ -388,3 +388,15 @@ def test_stream_read_reads_every_byte(nbytes):
         d2[pos] ^= 0x5A5A5A5A
         flipped = int(np.bitwise_xor.reduce(bi.bi_bench_stream_read(d2).cpu().numpy().view(np.uint32)))
         assert flipped == expect ^ 0x5A5A5A5A
+
+
+@pytest.mark.parametrize("rounds", [4, 64])
+def test_mfma_peak_runs_every_instruction(rounds):
+    """The MFMA throughput reference (measurement only): with all-one
+    fragments each MFMA adds 32 to every accumulator element, so each wave's
+    sink is 8 accumulators x 32 x rounds exactly, and the reported flop count
+    is waves x rounds x 8 x 16384."""
+    sink, flops = bi.bi_bench_mfma_peak(rounds, value=1.0)
+    got = sink.cpu().numpy()
+    assert np.all(got == 8.0 * 32.0 * rounds)
+    assert flops == got.size * rounds * 8 * 16384
