@@ -143,6 +143,8 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.bi_add_rmsnorm(FAKE, 4096, FAKE, 4000, FAKE, 4096, FAKE, 1e-5, 4, 4096, FAKE, 4096, None) == 1
     assert L.bi_add_rmsnorm(FAKE, 4096, FAKE, 4096, FAKE, 4096, FAKE, -1.0, 4, 4096, FAKE, 4096, None) == 1
     assert L.bi_add_rmsnorm(None, 4096, None, 4096, None, 4096, None, 1e-5, 0, 4096, None, 4096, None) == 0
+    assert L.bi_gemm(None, 4096, None, 4096, None, 14336, 0, 0, 14336, 4096, None) == 0   # M = 0: nothing to do
+    assert L.bi_gemm(None, 4096, None, 4096, None, 0, 1, 5, 0, 4096, None) == 0           # N = 0: nothing to do
     assert L.bi_gemm(FAKE, 4096, FAKE, 4096, FAKE, 14336, 0, 4, 14336, 4010, None) == 1   # K % 32
     assert L.bi_gemm(FAKE, 4096, FAKE, 4096, FAKE, 14336, 7, 4, 14336, 4096, None) == 1   # dtype
     assert L.bi_gemm(FAKE, 100, FAKE, 4096, FAKE, 14336, 0, 4, 14336, 4096, None) == 1    # lda < K

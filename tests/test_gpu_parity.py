@@ -164,6 +164,41 @@ def test_single_key_is_v0_bitwise():
         assert torch.equal(out[(rid, 0)].view(torch.int16), expect.view(torch.int16))
 
 
+@pytest.mark.parametrize("Hq,Hk,D", [(32, 8, 128), (8, 4, 256), (4, 2, 64)])
+def test_window_of_one_returns_own_value_bitwise(Hq, Hk, D):
+    """With a window of one key every row sees only its own position: one
+    score, weight exp(0) = 1, sum 1, so the output must be bf16(v_p) of the
+    row's KV head, bitwise, for prefill chunks and decode rows alike, at
+    positions deep inside long contexts (many splits before the window)."""
+    geom = synth.Geometry(Hq, Hk, D, 16)
+    cfg = bi.AttnConfig(Hq, Hk, D, split_size=256, window=1)
+    lengths = [700, 1300, 45]
+    reqs = {i: Request(820 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 180, seed=12)
+    run_step(kv, reqs, [(0, 600), (1, 1200), (2, 5)], attention=False)
+    out = run_step(kv, reqs, [(0, 99), (1, 37), (2, 39)])
+    out.update(run_step(kv, reqs, [(0, 1), (1, 1), (2, 1)]))
+    G = Hq // Hk
+    for (rid, p), row in out.items():
+        expect = reqs[rid].v[p].repeat_interleave(G, dim=0)
+        assert torch.equal(row.view(torch.int16), expect.view(torch.int16)), (rid, p)
+
+
+def test_gemma_shape_32k_context_decode_parity():
+    """The longest context of the decoder workload: a global (no window) layer
+    of the Gemma-shaped geometry decoding at position 32767 (128 splits per
+    row merged), next to a short sequence in the same batch."""
+    geom = synth.Geometry(8, 4, 256, 16)
+    cfg = bi.AttnConfig(8, 4, 256, split_size=256)
+    lengths = [32768, 300]
+    reqs = {i: Request(960 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 2100, seed=13)
+    run_step(kv, reqs, [(0, 32767), (1, 299)], attention=False)
+    out = run_step(kv, reqs, [(0, 1), (1, 1)])
+    ref = oracle_rows(reqs, list(out.keys()), geom, 0)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
 def test_split_phase_partials_parity():
     geom = synth.Geometry(4, 2, 64, 16)
     cfg = bi.AttnConfig(4, 2, 64, split_size=32)
