@@ -300,6 +300,22 @@ def test_rmsnorm_gemm_rows_independent_of_M(N, out_dtype):
                 assert first_mismatch(c[pos:pos + 1], single[r][1]) is None, (M, r)
 
 
+@pytest.mark.parametrize("N,K", [(20480, 2560), (2560, 10240), (2560, 2048), (4096, 2560)])
+def test_decoder_projection_rows_independent_of_M(N, K):
+    """The Gemma-shaped projections, whose tile configuration changes with M
+    (skinny, 32 x 80, 64 x 64, 128 x 160, 256 x 128 ...): every row of every M
+    equals that row computed alone, bit for bit."""
+    a = synth.normal_bf16_device((512, K), 611 + N % 97)
+    w = synth.normal_bf16_device((N, K), 612 + N % 89, std=0.02)
+    rows = [0, 3, 130, 255, 511]
+    single = {r: bi.bi_gemm(a[r:r + 1], w) for r in rows}
+    for M in (4, 16, 129, 200, 256, 300, 512):
+        c = bi.bi_gemm(a[:M], w)
+        for r in rows:
+            if r < M:
+                assert first_mismatch(c[r:r + 1], single[r]) is None, (N, K, M, r)
+
+
 # ---------------------------------------------------------------- positive controls
 
 def test_positive_control_splitk_attention_varies_with_batch():
