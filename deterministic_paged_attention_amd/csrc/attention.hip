@@ -825,22 +825,41 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
     return;
   }
   const float2* ml = a.ws_ml + row * a.ns;
+  const float* ap = a.ws_acc + row * a.ns * D + 4 * dq;
+  // The maximum: up to 32 splits' m loaded together per round (max is exact in
+  // any order, so the grouping changes no bit).
+  constexpr int kMaxGroup = 32, kSumGroup = 16;
   float mstar = -INFINITY;
-#pragma unroll 8
-  for (int sg = sig_lo; sg <= sig_hi; ++sg) mstar = fmaxf(mstar, ml[sg].x);
+  for (int base = sig_lo; base <= sig_hi; base += kMaxGroup) {
+    float mv[kMaxGroup];
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j) mv[j] = base + j <= sig_hi ? ml[base + j].x : -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMaxGroup; ++j) mstar = fmaxf(mstar, mv[j]);
+  }
+  // The sums, in increasing split order; the loads of up to 16 splits are
+  // issued before any of them is accumulated.
   float L = 0.f;
   f32x4 N = {0.f, 0.f, 0.f, 0.f};
-  const float* ap = a.ws_acc + row * a.ns * D + 4 * dq;
-  // Unrolled so the loads of several splits are in flight together; the
-  // accumulation itself stays in increasing split order.
-#pragma unroll 8
-  for (int sg = sig_lo; sg <= sig_hi; ++sg) {
-    const float2 v = ml[sg];
-    const float w = exp2_hw(v.x - mstar);
-    L = __builtin_fmaf(w, v.y, L);
-    const f32x4 av = *reinterpret_cast<const f32x4*>(ap + (int64_t)sg * D);
+  for (int base = sig_lo; base <= sig_hi; base += kSumGroup) {
+    float2 v[kSumGroup];
+    f32x4 av[kSumGroup];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) N[i] = __builtin_fmaf(w, av[i], N[i]);
+    for (int j = 0; j < kSumGroup; ++j) {
+      if (base + j <= sig_hi) {
+        v[j] = ml[base + j];
+        av[j] = *reinterpret_cast<const f32x4*>(ap + (int64_t)(base + j) * D);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < kSumGroup; ++j) {
+      if (base + j <= sig_hi) {
+        const float w = exp2_hw(v[j].x - mstar);
+        L = __builtin_fmaf(w, v[j].y, L);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) N[i] = __builtin_fmaf(w, av[j][i], N[i]);
+      }
+    }
   }
   bf16x4 o;
 #pragma unroll
