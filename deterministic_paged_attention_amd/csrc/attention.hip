@@ -80,7 +80,10 @@ __device__ __forceinline__ float row4_sum(float v) {
 }
 
 // Largest s with qsl[s] <= t.
-__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int t) {
+// (Every sequence has at least one query row, so when there are as many
+// tokens as sequences token t is sequence t's only row: no search.)
+__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int num_tokens, int t) {
+  if (num_tokens == num_seqs) return t;
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -811,7 +814,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   const int dq = (int)(gid % TPR);
   if (row >= (int64_t)a.num_tokens * a.num_q_heads) return;
   const int tok = (int)(row / a.num_q_heads);
-  const int s = find_token_seq(a.qsl, a.num_seqs, tok);
+  const int s = find_token_seq(a.qsl, a.num_seqs, a.num_tokens, tok);
   const int q0 = a.qsl[s];
   const int q_len = a.qsl[s + 1] - q0;
   const int k_len = a.seq_lens[s];

@@ -21,7 +21,10 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 __device__ __forceinline__ float bf16_to_f32(uint16_t v) { return __uint_as_float((uint32_t)v << 16); }
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) { return __builtin_bit_cast(uint16_t, (__bf16)f); }
 
-__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int t) {
+// (Every sequence has at least one query row, so when there are as many
+// tokens as sequences token t is sequence t's only row: no search.)
+__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int num_tokens, int t) {
+  if (num_tokens == num_seqs) return t;
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -128,7 +131,7 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_
     for (int d = lane; d < head_dim; d += 64) v_cache[base + v_elem(d, o)] = x[d];
     return;
   }
-  const int s = find_token_seq(qsl, num_seqs, t);
+  const int s = find_token_seq(qsl, num_seqs, num_tokens, t);
   const int p = seq_lens[s] - (qsl[s + 1] - qsl[s]) + (t - qsl[s]);
   uint16_t z[4];
   norm_rope_row(x, h < num_q_heads ? gamma_q : gamma_k, head_dim, p, eps, log2_theta, lane, z);

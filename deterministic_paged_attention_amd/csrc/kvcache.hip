@@ -14,7 +14,10 @@ namespace {
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
-__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int t) {
+// (Every sequence has at least one query row, so when there are as many
+// tokens as sequences token t is sequence t's only row: no search.)
+__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int num_tokens, int t) {
+  if (num_tokens == num_seqs) return t;
   int lo = 0, hi = num_seqs - 1;
   while (lo < hi) {
     const int mid = (lo + hi + 1) >> 1;
@@ -27,9 +30,9 @@ __device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, 
 // sequence s and logical position p = seq_lens[s] - q_len_s + j; -1 when the
 // entry is outside the table row or names no page of the pool.
 __device__ __forceinline__ int token_slot(const int32_t* page_table, int32_t stride, const int32_t* seq_lens,
-                                          const int32_t* qsl, int32_t num_seqs, int32_t page_size,
-                                          int32_t num_pages, int t) {
-  const int s = find_token_seq(qsl, num_seqs, t);
+                                          const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
+                                          int32_t page_size, int32_t num_pages, int t) {
+  const int s = find_token_seq(qsl, num_seqs, num_tokens, t);
   const int q0 = qsl[s];
   const int q_len = qsl[s + 1] - q0;
   const int p = seq_lens[s] - q_len + (t - q0);
@@ -51,7 +54,7 @@ __global__ __launch_bounds__(256) void slot_mapping_kernel(const int32_t* page_t
                                                            int32_t* slots) {
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= num_tokens) return;
-  slots[t] = token_slot(page_table, stride, seq_lens, qsl, num_seqs, page_size, num_pages, t);
+  slots[t] = token_slot(page_table, stride, seq_lens, qsl, num_seqs, num_tokens, page_size, num_pages, t);
 }
 
 // Where the cache write finds each token's slot: a slot mapping, or the page
@@ -63,8 +66,9 @@ struct SlotSource {
   const int32_t* seq_lens;
   const int32_t* qsl;
   int32_t num_seqs;
+  int32_t num_tokens;
   __device__ __forceinline__ int at(int t, int num_pages) const {
-    return slots ? slots[t] : token_slot(page_table, stride, seq_lens, qsl, num_seqs, 16, num_pages, t);
+    return slots ? slots[t] : token_slot(page_table, stride, seq_lens, qsl, num_seqs, num_tokens, 16, num_pages, t);
   }
 };
 
@@ -129,7 +133,7 @@ hipError_t launch_slot_mapping(const int32_t* page_table, int32_t stride, const 
 hipError_t launch_kv_write(int head_dim, int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
                            const uint16_t* v_new, int64_t v_stride, const int32_t* slots, int32_t num_tokens,
                            uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
-  const SlotSource src{slots, nullptr, 0, nullptr, nullptr, 0};
+  const SlotSource src{slots, nullptr, 0, nullptr, nullptr, 0, 0};
   switch (head_dim) {
     case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
     case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
@@ -142,7 +146,7 @@ hipError_t launch_kv_write_paged(int head_dim, int num_kv_heads, const uint16_t*
                                  const uint16_t* v_new, int64_t v_stride, const int32_t* page_table, int32_t stride,
                                  const int32_t* seq_lens, const int32_t* qsl, int32_t num_seqs, int32_t num_tokens,
                                  uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
-  const SlotSource src{nullptr, page_table, stride, seq_lens, qsl, num_seqs};
+  const SlotSource src{nullptr, page_table, stride, seq_lens, qsl, num_seqs, num_tokens};
   switch (head_dim) {
     case 64: return kv_write_launch<64>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
     case 128: return kv_write_launch<128>(num_kv_heads, k_new, k_stride, v_new, v_stride, src, num_tokens, k_cache, v_cache, num_pages, stream);
