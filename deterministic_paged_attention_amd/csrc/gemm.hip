@@ -222,10 +222,10 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, i
   // the next group; the last group of a slice is carried into the next
   // iteration, whose first reads (after the barrier) overlap it.  The carried
   // fragments start as zeros: their MFMAs add exact zeros to the zero
-  // accumulators (+0 + +0 = +0), which changes no bit.  Every element still sees one MFMA per
-  // K step, in increasing K.  The wait closes each group inside the iteration,
-  // so every copy the compiler makes of these registers (the loop-carried
-  // ones included) happens after their data has landed.
+  // accumulators (+0 + +0 = +0), which changes no bit.  Every element still
+  // sees one MFMA per K step, in increasing K.  The wait closes each group
+  // inside the iteration, so every copy the compiler makes of these registers
+  // (the loop-carried ones included) happens after their data has landed.
   u32x4 cw[GK * NB], ca[GK * MB];
 #pragma unroll
   for (int i = 0; i < GK * NB; ++i) cw[i] = u32x4{0u, 0u, 0u, 0u};
