@@ -42,6 +42,24 @@ def test_qk_norm_rope_at_position_zero_is_rmsnorm():
     np.testing.assert_array_equal(ko.reshape(8, 256), oracle.rmsnorm_ref(k.reshape(8, 256), gk, 1e-6))
 
 
+def test_golden_qk_norm_rope_norm_before_rotation():
+    """Hand-worked at p >= 1 with a non-uniform gain: rotating before the norm
+    (or dropping the norm, or the gain) fails it."""
+    g = load_golden("qk_norm_rope_hand.json")
+    q, k = g["q"], g["k"]
+    # two tokens: the q case at its position, the k case at its own
+    xq = np.asarray([[q["x"]], [q["x"]]])
+    xk = np.asarray([[k["x"]], [k["x"]]])
+    qo, ko = oracle.qk_norm_rope_ref(xq, xk, np.asarray(q["gamma"]), np.asarray(k["gamma"]), g["eps"],
+                                     [q["p"], k["p"]], g["theta"])
+    qo, ko = qo[:1], ko[1:]
+    np.testing.assert_allclose(qo[0, 0], q["expected"], rtol=0, atol=1e-14)
+    np.testing.assert_allclose(ko[0, 0], k["expected"], rtol=0, atol=1e-14)
+    # the swapped order is really distinguishable at these inputs
+    assert np.max(np.abs(np.asarray(q["expected"]) - q["rope_first"])) > 1e-2
+    assert np.max(np.abs(np.asarray(k["expected"]) - k["rope_first"])) > 1e-2
+
+
 def test_gelu_odd_part_limits_and_erf_form():
     x = np.linspace(-8, 8, 1601)
     g = oracle.gelu_tanh(x)

@@ -94,6 +94,15 @@ def test_golden_gemm():
                                   np.asarray(g["expected"], dtype=np.float64))
 
 
+def test_golden_gemm_abs_mixed_signs():
+    """Hand-worked sum_k |a w| with mixed signs: the signed product, or an
+    absolute value on one factor only, fails it."""
+    g = load_golden("gemm_abs_hand.json")
+    a, w = np.asarray(g["a"], dtype=np.float64), np.asarray(g["w"], dtype=np.float64)
+    np.testing.assert_array_equal(oracle.gemm_abs_ref(a, w), np.asarray(g["expected"], dtype=np.float64))
+    np.testing.assert_array_equal(oracle.gemm_ref(a, w), np.asarray(g["signed_product"], dtype=np.float64))
+
+
 def test_gemm_small_integers_exact_against_python_ints():
     a = synth.small_int_bf16((7, 40), 1)
     w = synth.small_int_bf16((9, 40), 2)
