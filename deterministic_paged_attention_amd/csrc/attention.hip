@@ -331,13 +331,18 @@ struct SeqSplits {
   int lo, n;  // first split meeting any row of the sequence, number of splits
 };
 
-__device__ __forceinline__ SeqSplits seq_splits(int q_len, int k_len, int window, int S) {
+// Splits are capped at ns, the workspace's splits per row (a length past the
+// max_seq_len the call was sized for is a precondition violation; the cap keeps
+// every partial store inside the row's ns slots, as the merge's cap keeps its
+// loads, and the result is truncated there).
+__device__ __forceinline__ SeqSplits seq_splits(int q_len, int k_len, int window, int S, int ns) {
   SeqSplits r{0, 0};
   if (q_len <= 0 || k_len <= 0 || q_len > k_len) return r;
   const int p_first = k_len - q_len;
   const int lo = window > 0 ? max(0, p_first - window + 1) : 0;
   r.lo = lo / S;
-  r.n = (k_len - 1) / S - r.lo + 1;
+  r.n = min((k_len - 1) / S, ns - 1) - r.lo + 1;
+  if (r.n <= 0) r = SeqSplits{0, 0};
   return r;
 }
 
@@ -355,7 +360,7 @@ __device__ __forceinline__ void plan_scan(const AttnSplitArgs& a, int* wave_tot,
     int c = 0;
     if (s < a.num_seqs) {
       const int q_len = a.qsl[s + 1] - a.qsl[s];
-      const SeqSplits sp = seq_splits(q_len, a.seq_lens[s], a.window, a.split);
+      const SeqSplits sp = seq_splits(q_len, a.seq_lens[s], a.window, a.split, a.ns);
       c = sp.n > 0 ? ((q_len + tq - 1) / tq) * a.num_kv_heads * sp.n : 0;
     }
     int incl = c;  // inclusive scan within the wave
@@ -422,7 +427,7 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, const PlanVi
   const int q0 = ldc(a.qsl, s);
   const int q_len = ldc(a.qsl, s + 1) - q0;
   const int k_len = ldc(a.seq_lens, s);
-  const SeqSplits sp = seq_splits(q_len, k_len, a.window, a.split);
+  const SeqSplits sp = seq_splits(q_len, k_len, a.window, a.split, a.ns);
   const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
   const int kvh = local % a.num_kv_heads;
   const int rest = local / a.num_kv_heads;

@@ -1,0 +1,267 @@
+"""The workload configurations at their stated sizes (GPU).
+
+* The headline 8B-shaped decode pool (256 requests, contexts U{512..8192}):
+  every row bitwise equal whether its request runs alone, in batches of 8, 64
+  or all 256, in any order, on relocated pages with wider page tables; and
+  every one of the 256 rows against the oracle.
+* The workgroup-shared (eight query blocks per item) and wide (four blocks)
+  prefill mappings against the oracle, row by row.
+* Chunked prefill with a shared 1024-token prefix: 8 requests with U{256..2048}
+  unique tokens, per-step budgets 16 / 128 / 512 in request order, one-shot and
+  token by token, shared and private prefix pages: every row produced by more
+  than one schedule, the final positions included, bitwise equal.
+* A length past the max_seq_len a call was sized for stays inside the
+  workspace.
+
+Variant classes follow the evaluation of the Vosti deep-dive blog
+(深入解析 Vosti), §7.1 (batch composition, chunking, prefill vs decode,
+prefix reuse); the fixed split size follows the record "Deterministic and
+bit-exact inference" (field technical, Invariance).
+"""
+import numpy as np
+import pytest
+import torch
+
+import deterministic_paged_attention_amd as bi
+import oracle
+import synth
+from harness import DEV, PagedKV, Request, first_mismatch, oracle_rows, page_table_tensor, run_step
+
+pytestmark = pytest.mark.gpu
+BF16_TOL = 2e-2
+LLAMA = synth.Geometry(32, 8, 128, 16)
+
+
+def _max_err(gpu_rows, ref_rows):
+    return max(float(np.max(np.abs(synth.to_f64(gpu_rows[k]) - ref_rows[k]))) for k in ref_rows)
+
+
+def _assert_same(a: dict, b: dict, what: str):
+    common = sorted(set(a) & set(b))
+    assert common, f"{what}: no common rows"
+    for k in common:
+        mm = first_mismatch(a[k], b[k])
+        assert mm is None, f"{what}: row {k} differs: {mm}"
+    return len(common)
+
+
+# ---------------------------------------------------------------- the headline decode pool
+
+@pytest.fixture(scope="module")
+def headline():
+    from synth.workloads import build_decode_workload
+    wl = build_decode_workload(32, 8, 128, batch=256, seed=2000)
+    torch.cuda.synchronize()
+    return wl
+
+
+def _relocate(wl, seed):
+    """The pool's pages moved to other physical pages: page p goes to pos[p] of a
+    fresh pool (an exact copy), and the page lists are rewritten accordingly."""
+    pos = synth.permutation(wl.num_pages, seed)
+    idx = torch.tensor(pos, dtype=torch.long, device=DEV)
+    k = torch.empty_like(wl.k_cache)
+    k.index_copy_(0, idx, wl.k_cache)
+    v = torch.empty_like(wl.v_cache)
+    v.index_copy_(0, idx, wl.v_cache)
+    return k, v, [[pos[p] for p in row] for row in wl.pages]
+
+
+def _decode_group(cfg, wl, k, v, pages, ids, stride_extra=0, fill=-1):
+    """One decode launch over the requests `ids` (in that order); {request: row}."""
+    sel = torch.tensor(ids, dtype=torch.long, device=DEV)
+    q = wl.q.index_select(0, sel).contiguous()
+    lens = [wl.lengths[i] for i in ids]
+    pt = page_table_tensor([pages[i] for i in ids], max(len(pages[i]) for i in ids) + stride_extra, fill).to(DEV)
+    sl = torch.tensor(lens, dtype=torch.int32, device=DEV)
+    qsl = torch.arange(len(ids) + 1, dtype=torch.int32, device=DEV)
+    out = bi.bi_paged_attention(cfg, q, k, v, pt, sl, qsl, max(lens))
+    return {i: out[j] for j, i in enumerate(ids)}
+
+
+def test_headline_pool_rows_bitwise_across_batch_sizes(headline):
+    """Batch 256 against batches of 64 and 8 (random compositions and orders),
+    32 requests alone, and batch 256 reversed: relocated pages, page tables
+    wider than needed with garbage past the used entries."""
+    wl = headline
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    ids = list(range(256))
+    ref = _decode_group(cfg, wl, wl.k_cache, wl.v_cache, wl.pages, ids)
+    k2, v2, pages2 = _relocate(wl, 7001)
+    n = _assert_same(ref, _decode_group(cfg, wl, k2, v2, pages2, ids[::-1], stride_extra=3, fill=10 ** 9),
+                     "batch 256 reversed, relocated")
+    assert n == 256
+    perm = synth.permutation(256, 7002)
+    for B, sx, fill in ((64, 1, -1), (8, 2, 123456)):
+        got = {}
+        for g in range(0, 256, B):
+            got.update(_decode_group(cfg, wl, k2, v2, pages2, perm[g:g + B], stride_extra=sx, fill=fill))
+        assert _assert_same(ref, got, f"batches of {B}") == 256
+    del k2, v2
+    # alone: the 16 longest, the 8 shortest and 8 others
+    by_len = sorted(ids, key=lambda i: wl.lengths[i])
+    alone_ids = by_len[-16:] + by_len[:8] + perm[:8]
+    got = {}
+    for i in dict.fromkeys(alone_ids):
+        got.update(_decode_group(cfg, wl, wl.k_cache, wl.v_cache, wl.pages, [i], stride_extra=1, fill=-5))
+    assert _assert_same(ref, got, "batch 1") >= 30
+
+
+def test_headline_pool_every_row_against_the_oracle(headline):
+    """All 256 rows of the batch-256 launch against the oracle (the launch the
+    bench times)."""
+    wl = headline
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    out = bi.bi_paged_attention(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                wl.max_seq_len).cpu()
+    q_all = synth.to_f64(wl.q.cpu())
+    worst = 0.0
+    for s in range(256):
+        kk, vv, table, L = wl.host_sequence(s)
+        ref = oracle.attention_ref(q_all[s:s + 1], kk, vv, table, [L], [0, 1], 8, 16)
+        worst = max(worst, float(np.max(np.abs(synth.to_f64(out[s:s + 1]) - ref))))
+    assert worst <= BF16_TOL, worst
+
+
+# ---------------------------------------------------------------- prefill mappings against the oracle
+
+@pytest.mark.parametrize("window", [0, 100])
+def test_shared_tile_items_against_the_oracle(window):
+    """A prefill step the launcher maps to workgroup-shared tiles (eight query
+    blocks per item): 300-token chunks at the end of four long requests."""
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256, window=window)
+    lengths = [900, 1100, 700, 1300]
+    reqs = {i: Request(1200 + i + window, L, LLAMA) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, sum(synth.pages_needed(L, 16) for L in lengths) + 9, seed=21)
+    run_step(kv, reqs, [(i, L - 300) for i, L in enumerate(lengths)], attention=False)
+    assert bi.bi_paged_attention_item_blocks(cfg, 4, 1200, max(lengths)) == 8
+    out = run_step(kv, reqs, [(i, 300) for i in range(4)])
+    assert len(out) == 1200
+    ref = oracle_rows(reqs, list(out.keys()), LLAMA, window)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+def test_shared_tile_items_head_dim_64_against_the_oracle():
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=256)
+    lengths = synth.uniform_ints(16, 560, 640, 1301)
+    reqs = {i: Request(1300 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, sum(synth.pages_needed(L, 16) for L in lengths) + 9, seed=22)
+    assert bi.bi_paged_attention_item_blocks(cfg, 16, sum(lengths), max(lengths)) == 8
+    out = run_step(kv, reqs, [(i, L) for i, L in enumerate(lengths)])
+    ref = oracle_rows(reqs, list(out.keys()), geom, 0)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+def test_wide_items_against_the_oracle():
+    """A step the launcher maps to four-block items: 24-token chunks at the end
+    of 48 requests of 520..700 tokens."""
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    lengths = synth.uniform_ints(48, 520, 700, 1401)
+    reqs = {i: Request(1400 + i, L, LLAMA) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, sum(synth.pages_needed(L, 16) for L in lengths) + 9, seed=23)
+    run_step(kv, reqs, [(i, L - 24) for i, L in enumerate(lengths)], attention=False)
+    assert bi.bi_paged_attention_item_blocks(cfg, 48, 24 * 48, max(lengths)) == 4
+    out = run_step(kv, reqs, [(i, 24) for i in range(48)])
+    ref = oracle_rows(reqs, list(out.keys()), LLAMA, 0)
+    assert _max_err(out, ref) <= BF16_TOL
+
+
+# ---------------------------------------------------------------- chunked prefill with a shared prefix
+
+PREFIX = 1024
+DECODE_TAIL = 16
+
+
+def _prefix_pool():
+    unique = synth.uniform_ints(8, 256, 2048, 2060)
+    return {i: Request(2061 + i, PREFIX + u, LLAMA, prefix_seed=2099, prefix_len=PREFIX) for i, u in enumerate(unique)}
+
+
+def _schedule_run(cfg, reqs, budget, shared, page_seed, stride_extra=0, fill=-1):
+    """Prompts (all but the last DECODE_TAIL tokens) under a per-step token
+    budget taken in request order (budget None: every prompt whole in one step;
+    budget 1: one token per live request per step), then DECODE_TAIL decode
+    steps of every request.  Shared: request 0 computes the prefix alone first
+    and the others start on its pages."""
+    n = len(reqs)
+    kv = PagedKV(cfg, sum(synth.pages_needed(r.length, 16) for r in reqs.values()) + 64, page_seed)
+    out = {}
+
+    def step(batch):
+        out.update(run_step(kv, reqs, batch, stride_extra=stride_extra, table_fill=fill))
+
+    if shared:
+        while kv.lens.get(0, 0) < PREFIX:
+            done = kv.lens.get(0, 0)
+            step([(0, PREFIX - done if budget is None else min(budget, PREFIX - done))])
+        for i in range(1, n):
+            kv.share(i, kv.tables[0][: PREFIX // 16], PREFIX)
+    prompt = {i: r.length - DECODE_TAIL for i, r in reqs.items()}
+    while True:
+        batch, left = [], budget
+        for i in range(n):
+            rem = prompt[i] - kv.lens.get(i, 0)
+            if rem <= 0:
+                continue
+            if budget is None:
+                batch.append((i, rem))
+            elif budget == 1:
+                batch.append((i, 1))
+            elif left > 0:
+                batch.append((i, min(left, rem)))
+                left -= batch[-1][1]
+        if not batch:
+            break
+        step(batch)
+    for _ in range(DECODE_TAIL):
+        step([(i, 1) for i in range(n)])
+    return out
+
+
+def test_prefix_sharing_schedules_at_full_size():
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256)
+    reqs = _prefix_pool()
+    total = sum(r.length for r in reqs.values())
+    ref = _schedule_run(cfg, reqs, None, shared=False, page_seed=1)            # private prefixes, one shot
+    assert len(ref) == total
+    finals = [(i, r.length - 1) for i, r in reqs.items()]
+    variants = [("budget 16, shared", 16, True, 2, 0, -1), ("budget 128, shared", 128, True, 3, 2, 77777),
+                ("budget 512, shared", 512, True, 4, 5, -1), ("token by token, private", 1, False, 5, 1, -1)]
+    for name, budget, shared, pseed, sx, fill in variants:
+        got = _schedule_run(cfg, reqs, budget, shared, pseed, sx, fill)
+        n = _assert_same(ref, got, name)
+        # shared schedules produce the prefix rows of request 0 only
+        assert n == (total - (len(reqs) - 1) * PREFIX if shared else total), name
+        assert all(k in got for k in finals), name
+
+
+# ---------------------------------------------------------------- precondition violation stays in bounds
+
+def test_length_past_max_seq_len_stays_inside_the_workspace():
+    """max_seq_len is documented as an upper bound of every length; a device
+    length past it (here 100 against 64) must still keep every partial store
+    inside the workspace (the split phase caps each row at the workspace's
+    splits, as the merge does), and rows within the bound are unaffected."""
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=32)
+    lengths = [100, 60]
+    reqs = {i: Request(1500 + i, L, geom) for i, L in enumerate(lengths)}
+    kv = PagedKV(cfg, 16, seed=24)
+    run_step(kv, reqs, [(0, 100), (1, 60)], attention=False)
+    pt = page_table_tensor([kv.tables[0], kv.tables[1]], 7).to(DEV)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    qsl = torch.tensor([0, 1, 2], dtype=torch.int32, device=DEV)
+    q = torch.stack([reqs[0].q[99], reqs[1].q[59]]).to(DEV)
+    need = bi.bi_paged_attention_workspace_size(cfg, 2, 2, 64)
+    guard = 1 << 16
+    buf = torch.full((need + guard,), 0xA5, dtype=torch.uint8, device=DEV)
+    out = torch.empty((2, 4, 64), dtype=torch.bfloat16, device=DEV)
+    lib = bi.lib
+    args = bi._attn_common(cfg, q, kv.k, kv.v, pt, sl, qsl)
+    bi._check(lib.bi_paged_attention(*args, 64, bi._ptr(buf), need, bi._ptr(out), bi._stream()))
+    torch.cuda.synchronize()
+    assert bool((buf[need:] == 0xA5).all()), "a store landed past the workspace"
+    alone = bi.bi_paged_attention(cfg, q[1:], kv.k, kv.v, pt[1:], sl[1:], torch.tensor([0, 1], dtype=torch.int32,
+                                                                                          device=DEV), 60)
+    assert first_mismatch(out[1:], alone) is None

@@ -275,8 +275,11 @@ def test_run_to_run_identical():
 
 # ---------------------------------------------------------------- RMSNorm + GEMM rows vs M
 
-@pytest.mark.parametrize("N,out_dtype", [(14336, torch.bfloat16), (8192, torch.float32)])
+@pytest.mark.parametrize("N,out_dtype", [(14336, torch.bfloat16), (8192, torch.float32), (128256, torch.float32)])
 def test_rmsnorm_gemm_rows_independent_of_M(N, out_dtype):
+    """Each M (1, 7, 64, 256, 1024) selects another kernel or tile bracket at
+    these widths, including the 128256-wide fp32 logits: every sampled row
+    equals that row computed alone, also with the rows permuted."""
     H = 4096
     x = synth.normal_bf16_device((1024, H), 601)
     g = synth.normal_bf16_device((H,), 602, std=0.1, mean=1.0)
