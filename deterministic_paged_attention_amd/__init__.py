@@ -72,6 +72,7 @@ _sig("bi_paged_attention_item_blocks", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
+_sig("bi_paged_attention_noalloc", c_i32, *_ATTN_ARGS, c_vp, c_vp)
 _sig("bi_paged_attention_merge", c_i32, c_vp, c_vp, c_vp, c_i32, c_i32, c_i32, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c_vp)
 _sig("bi_gemm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i32, c_i64, c_i64, c_i64, c_vp)
@@ -286,6 +287,19 @@ def bi_paged_attention(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_len
         out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
     _check(lib.bi_paged_attention(*args, max_seq_len, _ptr(workspace), workspace.numel() * workspace.element_size(),
                                   _ptr(out), _stream(stream)))
+    return out
+
+
+def bi_paged_attention_noalloc(cfg: AttnConfig, q, k_cache, v_cache, page_table, seq_lens, query_start_loc,
+                               max_seq_len, out=None, stream=None):
+    """bi_paged_attention with the partials in the library's own device array
+    (no workspace; the caller passes inputs and the output)."""
+    torch = _torch()
+    args = _attn_common(cfg, q, k_cache, v_cache, page_table, seq_lens, query_start_loc)
+    T = q.shape[0]
+    if out is None:
+        out = torch.empty((T, cfg.num_q_heads, cfg.head_dim), dtype=torch.bfloat16, device=q.device)
+    _check(lib.bi_paged_attention_noalloc(*args, max_seq_len, _ptr(out), _stream(stream)))
     return out
 
 

@@ -12,6 +12,7 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <vector>
@@ -421,6 +422,74 @@ bi_status bi_paged_attention(const bi_attn_config* cfg, const void* q_dev, int64
     return st;
   return run_merge(cfg, seq_lens_dev, query_start_loc_dev, num_seqs, num_tokens, cfg->desc.split_size, ns,
                    workspace_dev, workspace_bytes, out_dev, (hipStream_t)stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// Allocation-free paged attention: the partials live in a file-scope device
+// array instead of a caller workspace.  Each GPU the library runs on holds its
+// own copy of the array (kNoallocScratchBytes, until the process ends); the
+// host name `scratch` is only a stand-in for it, so the device address is
+// looked up once per device (with that device current) and only that address
+// is ever handed to a kernel.
+// ---------------------------------------------------------------------------
+namespace {
+
+constexpr size_t kNoallocScratchBytes = size_t(64) << 20;
+constexpr int kMaxDevices = 64;
+
+static __device__ __align__(256) unsigned char scratch[kNoallocScratchBytes];
+
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+
+// Device address of this device's scratch array (nullptr with the HIP error on failure).
+void* device_scratch(int dev, hipError_t* err) {
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    g_scratch_err[dev] = e;
+    g_scratch_ptr[dev] = e == hipSuccess ? ptr : nullptr;
+  });
+  *err = g_scratch_err[dev];
+  return g_scratch_ptr[dev];
+}
+
+}  // namespace
+
+extern "C" {
+
+bi_status bi_paged_attention_noalloc(const bi_attn_config* cfg, const void* q_dev, int64_t q_row_stride,
+                                     const void* k_cache_dev, const void* v_cache_dev, int32_t num_pages,
+                                     const int32_t* page_table_dev, int32_t page_table_stride,
+                                     const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len, void* out_dev,
+                                     void* stream) {
+  const AttnCall c{q_dev, q_row_stride, k_cache_dev, v_cache_dev, num_pages, page_table_dev, page_table_stride,
+                   seq_lens_dev, query_start_loc_dev, num_seqs, num_tokens, max_seq_len};
+  if (bi_status st = check_attn_call(cfg, c)) return st;
+  if (num_tokens > 0 && !out_dev) return fail(BI_ERR_INVALID_ARG, "out is NULL");
+  const int32_t ns = fixed_ns(cfg, max_seq_len);
+  const size_t need =
+      ws_layout(cfg->desc.head_dim, (int64_t)num_tokens * cfg->desc.num_q_heads, ns, num_seqs).total;
+  if (need > kNoallocScratchBytes)
+    return fail(BI_ERR_WORKSPACE_TOO_SMALL,
+                "this call needs %zu bytes of partials; the allocation-free entry point holds at most %zu "
+                "(use bi_paged_attention with a workspace)",
+                need, kNoallocScratchBytes);
+  if (num_tokens == 0) return ok();
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices)
+    return fail(BI_ERR_HIP, "no usable current device");
+  hipError_t e = hipSuccess;
+  void* ws = device_scratch(dev, &e);
+  if (!ws) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e, "scratch symbol lookup");
+  if (bi_status st = run_split(cfg, c, cfg->desc.split_size, ns, ws, kNoallocScratchBytes, (hipStream_t)stream))
+    return st;
+  return run_merge(cfg, seq_lens_dev, query_start_loc_dev, num_seqs, num_tokens, cfg->desc.split_size, ns, ws,
+                   kNoallocScratchBytes, out_dev, (hipStream_t)stream);
 }
 
 bi_status bi_splitk_attention_heuristic(const bi_attn_config* cfg, int32_t num_seqs, int32_t max_seq_len,

@@ -179,6 +179,29 @@ bi_status bi_paged_attention(const bi_attn_config* cfg,
                              void* workspace_dev, size_t workspace_bytes,
                              void* out_dev, void* stream);
 
+/* bi_paged_attention without a workspace, for callers that cannot allocate
+ * device memory (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  The split partials and the work plan live in a
+ * device array inside the library, 64 MiB on each GPU the library runs on,
+ * held until the process ends; a call whose workspace would exceed it
+ * (bi_paged_attention_workspace_size > 64 MiB) returns
+ * BI_ERR_WORKSPACE_TOO_SMALL and launches nothing.  Nothing here allocates:
+ * the array's device address is looked up once per device, on the first call
+ * made with that device current.  Every call on one GPU shares that GPU's
+ * array, and the array keeps the last call's contents (each call writes every
+ * partial it reads, so no clearing is needed): calls that overlap on one GPU
+ * (concurrent streams, or host threads sharing the device) race and must be
+ * serialised by the caller.  Arguments, results and errors are otherwise
+ * those of bi_paged_attention; the output is bitwise that of
+ * bi_paged_attention for the same arguments. */
+bi_status bi_paged_attention_noalloc(const bi_attn_config* cfg,
+                                     const void* q_dev, int64_t q_row_stride,
+                                     const void* k_cache_dev, const void* v_cache_dev, int32_t num_pages,
+                                     const int32_t* page_table_dev, int32_t page_table_stride,
+                                     const int32_t* seq_lens_dev, const int32_t* query_start_loc_dev,
+                                     int32_t num_seqs, int32_t num_tokens, int32_t max_seq_len,
+                                     void* out_dev, void* stream);
+
 /* Work mapping of the split phase (diagnostic).  A work item is one
  * (sequence, group of query-row blocks, KV head, split); *blocks receives the
  * number of 16-column query-row blocks per item the split phase would use for

@@ -133,6 +133,23 @@ def test_attention_rejects_bad_arguments(kw, status):
     assert bi.lib.bi_last_error_message().decode() != ""
 
 
+def test_noalloc_attention_rejects_before_any_launch():
+    """The allocation-free entry point refuses a call whose partials exceed its
+    64 MiB device array (the 8B decode at 256 sequences of up to 8192 keys needs
+    about 136 MB) and bad arguments, before touching the device."""
+    cfg = bi.AttnConfig(32, 8, 128)
+    L = bi.lib
+    args = (cfg.handle, FAKE, 32 * 128, FAKE, FAKE, 10, FAKE, 512, FAKE, FAKE)
+    assert bi.bi_paged_attention_workspace_size(cfg, 256, 256, 8192) > 64 << 20
+    assert L.bi_paged_attention_noalloc(*args, 256, 256, 8192, FAKE, None) == 5
+    assert "64" in bi.lib.bi_last_error_message().decode() or "67108864" in bi.lib.bi_last_error_message().decode()
+    assert L.bi_paged_attention_noalloc(*args, 2, 2, 64, None, None) == 1            # no output
+    assert L.bi_paged_attention_noalloc(*args, 0, 2, 64, FAKE, None) == 1            # no sequences
+    assert L.bi_paged_attention_noalloc(cfg.handle, FAKE, 100, FAKE, FAKE, 10, FAKE, 512, FAKE, FAKE, 2, 2, 64, FAKE,
+                                        None) == 1                                    # q row stride < H_q * D
+    assert L.bi_paged_attention_noalloc(*args, 2, 0, 64, None, None) == 0             # no tokens: nothing to do
+
+
 def test_other_entry_points_reject_bad_arguments():
     L = bi.lib
     assert L.bi_rmsnorm(FAKE, 4096, FAKE, 1e-5, 4, 4100, FAKE, 4096, None) == 1      # H not multiple of 8
