@@ -2,14 +2,15 @@
 """Benchmark: one batch-invariant decode step of a Llama-3.1-8B-shaped attention layer.
 
 Step (every row of the hot path, on one batch of synthetic input resident in HBM):
-  RMSNorm(x) -> QKV GEMM [B,4096]x[6144,4096]^T -> slot mapping -> KV write of the
-  new token -> paged attention split phase -> merge phase -> O GEMM [B,4096]x[4096,4096]^T
+  RMSNorm(x) -> QKV GEMM [B,4096]x[6144,4096]^T -> slot mapping + KV write of the
+  new token -> paged attention (split phase and fixed-order merge; at this batch one
+  launch of the row-group mapping) -> O GEMM [B,4096]x[4096,4096]^T
 Geometry: 32 query / 8 KV heads, head_dim 128, pages of 16 tokens, fixed key split
 256, context lengths ~ U{512..8192}, K/V/x ~ N(0,1) bf16, weights ~ N(0, 0.02),
 gamma ~ N(1, 0.1).  Random-init, synthetic data.
 
 Prints ONE JSON line.  `value` = algorithmic HBM bytes of the whole step / step
-time (GB/s).  `roofline` is for the dominant kernel (attention split phase),
+time (GB/s).  `roofline` is for the dominant kernel (the attention launch),
 timed with HIP events recorded on the stream it is launched on.
 `cpu_baseline` times the CPU oracle on a bounded sample of the same workload.
 
@@ -212,27 +213,30 @@ def bench_decode(args):
     ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, B, wl.max_seq_len))
     stream = torch.cuda.current_stream()
 
-    # slot mapping + KV write as one launch (bi_kv_write_paged: slots from the page table)
-    names = ["rmsnorm", "gemm_qkv", "kv_write", "attn_split", "attn_merge", "gemm_o"]
+    # slot mapping + KV write as one launch (bi_kv_write_paged: slots from the page table);
+    # attention through bi_paged_attention, which runs the row-group mapping (split
+    # and merge in one launch, partials in LDS) for a batch that fills the GPU, else
+    # the split and merge phases
+    mapping = bi.bi_paged_attention_mapping(cfg, B, B, wl.max_seq_len)
+    names = ["rmsnorm", "gemm_qkv", "kv_write", "attention", "gemm_o"]
     launches = [
         lambda: bi.bi_rmsnorm(x, gamma, 1e-5, out=xn),
         lambda: bi.bi_gemm(xn, w_qkv, out=qkv),
         lambda: bi.bi_kv_write_paged(cfg, k_new, v_new, wl.page_table, wl.seq_lens, wl.qsl, wl.k_cache, wl.v_cache),
-        lambda: bi.bi_paged_attention_split(cfg, q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
-                                            wl.max_seq_len, ws),
-        lambda: bi.bi_paged_attention_merge(cfg, wl.seq_lens, wl.qsl, B, wl.max_seq_len, ws, out=attn),
+        lambda: bi.bi_paged_attention(cfg, q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                      wl.max_seq_len, workspace=ws, out=attn),
         lambda: bi.bi_gemm(attn.view(B, HQ * D), w_o, out=y),
     ]
 
-    SPLIT = names.index("attn_split")
+    ATTN = names.index("attention")
 
     def step(events=None):
-        """One decode step.  events: (before, after) the split kernel, on its stream."""
+        """One decode step.  events: (before, after) the attention launch(es), on their stream."""
         for i, f in enumerate(launches):
-            if events is not None and i == SPLIT:
+            if events is not None and i == ATTN:
                 events[0].record(stream)
             f()
-            if events is not None and i == SPLIT:
+            if events is not None and i == ATTN:
                 events[1].record(stream)
 
     for _ in range(args.warmup):
@@ -252,7 +256,7 @@ def bench_decode(args):
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
     ms_per_step = total_ms / args.steps
-    split_us = statistics.mean(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) * 1e3
+    attn_launch_us = statistics.mean(ev[k][0].elapsed_time(ev[k][1]) for k in range(args.steps)) * 1e3
 
     # Per-kernel breakdown, after the timed region: events around every launch.
     bev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(launches) + 1)] for _ in range(args.steps)]
@@ -265,11 +269,13 @@ def bench_decode(args):
     per_kernel = {n: statistics.mean(bev[k][i].elapsed_time(bev[k][i + 1]) for k in range(args.steps)) * 1e3
                   for i, n in enumerate(names)}
 
-    sb = split_bytes(lengths)
-    achieved = sb / (split_us * 1e-6) / 1e9
+    # Algorithmic bytes of the attention launch: K+V of every visible key, Q,
+    # page-table entries, and the output rows.
+    sb = split_bytes(lengths) + B * HQ * D * 2
+    achieved = sb / (attn_launch_us * 1e-6) / 1e9
     value = step_bytes(lengths) / (ms_per_step * 1e-3) / 1e9
-    attn_us = per_kernel["attn_split"] + per_kernel["attn_merge"]
-    attn_gbps = (sb + B * HQ * D * 2) / (attn_us * 1e-6) / 1e9
+    attn_us = per_kernel["attention"]
+    attn_gbps = sb / (attn_us * 1e-6) / 1e9
 
     splitk = None
     if not args.no_splitk:
@@ -282,8 +288,7 @@ def bench_decode(args):
         out_k = torch.empty_like(attn)
 
         def run_inv():
-            launches[SPLIT]()
-            launches[SPLIT + 1]()
+            launches[ATTN]()
 
         def splitk_runner(n):
             ws_k = bi.alloc_workspace(bi.bi_paged_attention_splitk_workspace_size(cfg, B, B, wl.max_seq_len, n))
@@ -348,8 +353,10 @@ def bench_decode(args):
                    "hidden": HIDDEN, "parallelism": "single GPU"},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 2), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(achieved / PEAK_HBM_GBPS, 4), "traffic": measured_traffic(B),
-                     "kernel": "attn_split_kernel<128, 1>", "algorithmic_bytes_per_launch": sb,
-                     "avg_launch_us": round(split_us, 2),
+                     "kernel": "attn_rowgroup_kernel<128>" if mapping == 1 else
+                               "attn_split_kernel<128, 1> + attn_merge_kernel<128>",
+                     "algorithmic_bytes_per_launch": sb,
+                     "avg_launch_us": round(attn_launch_us, 2), "mapping": "row-group" if mapping == 1 else "split + merge",
                      "measured_stream_read_gbps": read_ref["gbps"],
                      "frac_of_measured_stream_read": round(achieved / read_ref["gbps"], 4)},
         "cpu_baseline": cpu,
@@ -420,9 +427,10 @@ def blas_threads():
 
 
 def bench_decode_sweep(args):
-    """Attention split + merge of the 8B-shaped decode layer at batch 1, 8, 64 and
-    256 (the first B sequences of one 256-sequence pool), MALL flushed before each
-    repetition, against the fastest split-K split count."""
+    """Batch-invariant attention (bi_paged_attention: the split and merge phases, or
+    the row-group mapping once the batch fills the GPU) of the 8B-shaped decode layer
+    at batch 1, 8, 64 and 256 (the first B sequences of one 256-sequence pool), MALL
+    flushed before each repetition, against the fastest split-K split count."""
     torch, bi, synth = _torch_env()
     from synth.workloads import build_decode_workload
     cfg = bi.AttnConfig(HQ, HKV, D, page_size=P, split_size=S)
@@ -437,9 +445,8 @@ def bench_decode_sweep(args):
         out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
 
         def inv():
-            bi.bi_paged_attention_split(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
-                                        wl.max_seq_len, ws)
-            bi.bi_paged_attention_merge(cfg, wl.seq_lens, wl.qsl, B, wl.max_seq_len, ws, out=out)
+            bi.bi_paged_attention(cfg, wl.q, wl.k_cache, wl.v_cache, wl.page_table, wl.seq_lens, wl.qsl,
+                                  wl.max_seq_len, workspace=ws, out=out)
         inv()
         t_inv = pct(rep_times_ms(inv, reps, flush))
         heur = bi.bi_splitk_attention_heuristic(cfg, B, wl.max_seq_len, props.multi_processor_count, 8)
@@ -456,7 +463,9 @@ def bench_decode_sweep(args):
         best = min(per_n, key=per_n.get)
         nbytes = split_bytes(wl.lengths) + B * HQ * D * 2
         gbps = nbytes / (t_inv["median"] * 1e-3) / 1e9
-        rows.append({"batch": B, "algorithmic_bytes": nbytes, "invariant_ms": {k: round(v, 4) for k, v in t_inv.items()},
+        mapping = bi.bi_paged_attention_mapping(cfg, B, B, wl.max_seq_len)
+        rows.append({"batch": B, "mapping": "row-group" if mapping == 1 else "split + merge",
+                     "algorithmic_bytes": nbytes, "invariant_ms": {k: round(v, 4) for k, v in t_inv.items()},
                      "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                      "splitk_ms": round(per_n[best], 4), "splitk_num_splits": best, "heuristic_num_splits": heur,
                      "overhead_vs_splitk": round(t_inv["median"] / per_n[best] - 1.0, 4)})

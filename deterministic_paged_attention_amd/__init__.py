@@ -69,6 +69,7 @@ _sig("bi_kv_write_paged", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_
      c_vp)
 _sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_item_blocks", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
+_sig("bi_paged_attention_mapping", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
@@ -336,6 +337,13 @@ def workspace_views(cfg: AttnConfig, workspace, num_tokens: int, num_splits: int
 def bi_paged_attention_item_blocks(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int) -> int:
     v = c_i32()
     _check(lib.bi_paged_attention_item_blocks(cfg.handle, num_seqs, num_tokens, max_seq_len, ctypes.byref(v)))
+    return v.value
+
+
+def bi_paged_attention_mapping(cfg: AttnConfig, num_seqs: int, num_tokens: int, max_seq_len: int) -> int:
+    """1 when bi_paged_attention runs the row-group mapping for this batch shape, else 0."""
+    v = c_i32()
+    _check(lib.bi_paged_attention_mapping(cfg.handle, num_seqs, num_tokens, max_seq_len, ctypes.byref(v)))
     return v.value
 
 

@@ -286,6 +286,26 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
   return ok();
 }
 
+bi_status bi_paged_attention_mapping(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t max_seq_len, int32_t* mapping) {
+  if (bi_status st = check_cfg(cfg)) return st;
+  if (!mapping || num_seqs < 1 || num_tokens < 0 || max_seq_len < 1)
+    return fail(BI_ERR_INVALID_ARG, "mapping NULL, num_seqs < 1, num_tokens < 0 or max_seq_len < 1");
+  bi::AttnSplitArgs a{};
+  a.num_seqs = num_seqs;
+  a.num_tokens = num_tokens;
+  a.num_q_heads = cfg->desc.num_q_heads;
+  a.num_kv_heads = cfg->desc.num_kv_heads;
+  a.log2_group = cfg->log2_group;
+  a.split = cfg->desc.split_size;
+  a.window = cfg->desc.window;
+  a.ns = (int32_t)((max_seq_len + (int64_t)cfg->desc.split_size - 1) / cfg->desc.split_size);
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(BI_ERR_HIP, "no usable device to size the launch");
+  *mapping = bi::attn_rowgroup_applies(cfg->desc.head_dim, a) ? 1 : 0;
+  return ok();
+}
+
 bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                                    int32_t max_seq_len, int32_t num_splits, size_t* bytes) {
   if (bi_status st = check_cfg(cfg)) return st;
@@ -299,8 +319,12 @@ bi_status bi_paged_attention_splitk_workspace_size(const bi_attn_config* cfg, in
 
 namespace {
 
+// The split phase; with `fused` non-null (the invariant path of
+// bi_paged_attention, output `out`), a decode batch that the row-group mapping
+// covers runs split and merge in one launch instead, and *fused is set.
 bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split, int32_t ns, void* ws, size_t ws_bytes,
-                    hipStream_t stream) {
+                    hipStream_t stream, void* out = nullptr, bool* fused = nullptr) {
+  if (fused) *fused = false;
   const WsLayout L = ws_layout(cfg->desc.head_dim, (int64_t)c.num_tokens * cfg->desc.num_q_heads, ns, c.num_seqs);
   if (!ws && L.total) return fail(BI_ERR_INVALID_ARG, "workspace is NULL");
   if (ws_bytes < L.total)
@@ -339,6 +363,11 @@ bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split,
   a.ws_ml = (float2*)ws;
   a.ws_acc = (float*)((char*)ws + L.acc_offset);
   a.plan = (int32_t*)((char*)ws + L.plan_offset);
+  a.out = (uint16_t*)out;
+  if (fused && out && aligned(out, 8) && bi::attn_rowgroup_applies(cfg->desc.head_dim, a)) {
+    *fused = true;
+    return hip_status(bi::launch_attn_rowgroup(cfg->desc.head_dim, a, stream), "attention row-group launch");
+  }
   return hip_status(bi::launch_attn_split(cfg->desc.head_dim, a, stream), "attention split launch");
 }
 
@@ -418,8 +447,11 @@ bi_status bi_paged_attention(const bi_attn_config* cfg, const void* q_dev, int64
   if (bi_status st = check_attn_call(cfg, c)) return st;
   if (num_tokens > 0 && !out_dev) return fail(BI_ERR_INVALID_ARG, "out is NULL");
   const int32_t ns = fixed_ns(cfg, max_seq_len);
-  if (bi_status st = run_split(cfg, c, cfg->desc.split_size, ns, workspace_dev, workspace_bytes, (hipStream_t)stream))
+  bool fused = false;
+  if (bi_status st = run_split(cfg, c, cfg->desc.split_size, ns, workspace_dev, workspace_bytes, (hipStream_t)stream,
+                               out_dev, &fused))
     return st;
+  if (fused) return ok();
   return run_merge(cfg, seq_lens_dev, query_start_loc_dev, num_seqs, num_tokens, cfg->desc.split_size, ns,
                    workspace_dev, workspace_bytes, out_dev, (hipStream_t)stream);
 }
@@ -486,8 +518,11 @@ bi_status bi_paged_attention_noalloc(const bi_attn_config* cfg, const void* q_de
   hipError_t e = hipSuccess;
   void* ws = device_scratch(dev, &e);
   if (!ws) return hip_status(e == hipSuccess ? hipErrorInvalidSymbol : e, "scratch symbol lookup");
-  if (bi_status st = run_split(cfg, c, cfg->desc.split_size, ns, ws, kNoallocScratchBytes, (hipStream_t)stream))
+  bool fused = false;
+  if (bi_status st =
+          run_split(cfg, c, cfg->desc.split_size, ns, ws, kNoallocScratchBytes, (hipStream_t)stream, out_dev, &fused))
     return st;
+  if (fused) return ok();
   return run_merge(cfg, seq_lens_dev, query_start_loc_dev, num_seqs, num_tokens, cfg->desc.split_size, ns, ws,
                    kNoallocScratchBytes, out_dev, (hipStream_t)stream);
 }

@@ -411,6 +411,29 @@ struct Item {
   const int32_t* pt_row;
 };
 
+// The item (sequence s, KV head kvh, split sigma, query tokens [tq0, tq0 + tq)
+// of the sequence's q_len): its rows' positions and the tiles of the split
+// that any of them sees.
+__device__ __forceinline__ void fill_item(const AttnSplitArgs& a, Item& it, int s, int kvh, int sigma, int q0,
+                                          int q_len, int k_len, int tq0, int tq) {
+  it.s = s;
+  it.kvh = kvh;
+  it.sigma = sigma;
+  it.q0 = q0;
+  it.tq0 = tq0;
+  it.nrow_tok = min(tq, q_len - it.tq0);
+  it.k_len = k_len;
+  it.p_first = k_len - q_len + it.tq0;
+  const int p_last = it.p_first + it.nrow_tok - 1;
+  const int lo_first = a.window > 0 ? max(0, it.p_first - a.window + 1) : 0;
+  const int key_begin = max(sigma * a.split, lo_first);
+  const int key_end = min(sigma * a.split + a.split, p_last + 1);
+  it.tile_begin = key_begin < key_end ? (key_begin >> 5) : (sigma * a.split) >> 5;
+  it.tile_end = key_begin < key_end ? ((key_end + 31) >> 5) : it.tile_begin + 1;
+  it.last_entry = max(0, min((k_len + 15) / 16, a.pt_stride) - 1);
+  it.pt_row = a.page_table + (int64_t)s * a.pt_stride;
+}
+
 __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, const PlanView& pv, int u, int total) {
   Item it;
   it.valid = u < total;
@@ -431,23 +454,7 @@ __device__ __forceinline__ Item decode_item(const AttnSplitArgs& a, const PlanVi
   const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
   const int kvh = local % a.num_kv_heads;
   const int rest = local / a.num_kv_heads;
-  const int sigma = sp.lo + rest % sp.n;
-  it.s = s;
-  it.kvh = kvh;
-  it.sigma = sigma;
-  it.q0 = q0;
-  it.tq0 = (rest / sp.n) * tq;
-  it.nrow_tok = min(tq, q_len - it.tq0);
-  it.k_len = k_len;
-  it.p_first = k_len - q_len + it.tq0;
-  const int p_last = it.p_first + it.nrow_tok - 1;
-  const int lo_first = a.window > 0 ? max(0, it.p_first - a.window + 1) : 0;
-  const int key_begin = max(sigma * a.split, lo_first);
-  const int key_end = min(sigma * a.split + a.split, p_last + 1);
-  it.tile_begin = key_begin < key_end ? (key_begin >> 5) : (sigma * a.split) >> 5;
-  it.tile_end = key_begin < key_end ? ((key_end + 31) >> 5) : it.tile_begin + 1;
-  it.last_entry = max(0, min((k_len + 15) / 16, a.pt_stride) - 1);
-  it.pt_row = a.page_table + (int64_t)s * a.pt_stride;
+  fill_item(a, it, s, kvh, sp.lo + rest % sp.n, q0, q_len, k_len, (rest / sp.n) * tq, tq);
   return it;
 }
 
@@ -806,6 +813,27 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
 }
 
 // ---------------------------------------------------------------------------
+// Merge arithmetic of one row's four head-dim values, shared by the merge
+// kernel and the row-group decode kernel so that both give the same bits:
+// after m* = max_s m_s (exact in any order), splits are folded in increasing
+// order, w = 2^(m_s - m*), L += w l_s, N += w acc_s (one fma each); then
+// o = N / L, -0 stored as +0, rounded to bf16.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void merge_fold(float mstar, float2 ml, const f32x4& acc, float& L, f32x4& N) {
+  const float w = exp2_hw(ml.x - mstar);
+  L = __builtin_fmaf(w, ml.y, L);
+#pragma unroll
+  for (int i = 0; i < 4; ++i) N[i] = __builtin_fmaf(w, acc[i], N[i]);
+}
+
+__device__ __forceinline__ u32x2 merge_finish(const f32x4& N, float L) {
+  bf16x4 o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) o[i] = (__bf16)(N[i] / L + 0.0f);
+  return __builtin_bit_cast(u32x2, o);
+}
+
+// ---------------------------------------------------------------------------
 // Merge phase: one thread per (row, 4 head-dim elements).  Splits are combined
 // in increasing order: m* = max m_s, w_s = 2^(m_s - m*), L = sum w_s l_s,
 // N = sum w_s acc_s, o = N / L.  With a single split w = 1 exactly and the
@@ -860,19 +888,339 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
       }
     }
 #pragma unroll
-    for (int j = 0; j < kSumGroup; ++j) {
-      if (base + j <= sig_hi) {
-        const float w = exp2_hw(v[j].x - mstar);
-        L = __builtin_fmaf(w, v[j].y, L);
-#pragma unroll
-        for (int i = 0; i < 4; ++i) N[i] = __builtin_fmaf(w, av[j][i], N[i]);
+    for (int j = 0; j < kSumGroup; ++j)
+      if (base + j <= sig_hi) merge_fold(mstar, v[j], av[j], L, N);
+  }
+  *reinterpret_cast<u32x2*>(op) = merge_finish(N, L);
+}
+
+// ---------------------------------------------------------------------------
+// Decode, row-group mapping: split and merge in one launch, partials in LDS.
+//
+// A row group is one (sequence, KV head) of a decode batch: the G query heads
+// that read that KV head, one row each.  Its tasks are its splits, and a task
+// is exactly a work item of the split kernel (the same tile range, load_tile,
+// compute_tile, one query-row block), so each split's (m, l, acc) has the same
+// bits.  The partial goes to an LDS ring instead of the workspace, and the wave
+// that completes a row group's last split folds its partials with the merge
+// kernel's arithmetic (merge_fold, merge_finish, splits in increasing order)
+// and writes the G output rows: the output is bitwise that of split + merge.
+//
+// Work distribution (it changes no bit).  Each workgroup (one per CU, eight
+// waves) ranks the sequences by visible keys, most first, ties by index; the
+// row groups in that order are dealt to the workgroups in a snake (forward in
+// even rounds, backward in odd ones), so totals come out close.  Inside a
+// workgroup the tasks of its row groups, in order, are claimed one at a time
+// from an LDS counter; a wave claims its next task when it starts one, so the
+// next task's first tile loads while the current one's last tile is computed.
+//
+// Ring protocol.  The workgroup's task j writes its partial to ring entry
+// j mod C once gen[j mod C] == j / C, i.e. once the row group of task j - C
+// has been merged; a merge raises the generation of the entries it read.  A
+// row group's tasks are consecutive and the launcher takes this mapping only
+// when every row group has at most C splits, so every task a waiting wave
+// depends on precedes its own and is held by a wave that is not waiting: each
+// wait ends.  Each is bounded all the same (a wrong count ends the wait
+// instead of hanging the kernel).
+// ---------------------------------------------------------------------------
+constexpr int kRgWaves = 8;
+constexpr int kRgMaxSeqs = 2048;        // sequences ranked in LDS
+constexpr int kRgMaxGroups = 64;        // row groups per workgroup
+constexpr int kRgRingBytes = 120 * 1024;
+constexpr int kRgMaxEntries = 256;
+// Polls of one ring entry (each after a short sleep): about a millisecond, far
+// beyond any legitimate wait (a few tasks of other waves).  After one wait has
+// run out the workgroup stops waiting altogether, so a broken count costs at
+// most that once.
+constexpr int kRgSpinLimit = 1 << 14;
+
+// Ring entry of one task: acc float [G][D], then (m, l) float2 [G]; 16-byte multiple.
+__host__ __device__ inline int rg_entry_bytes(int D, int G) { return (G * (4 * D + 8) + 15) & ~15; }
+__host__ __device__ inline int rg_entries(int D, int G) {
+  const int c = kRgRingBytes / rg_entry_bytes(D, G);
+  return c < kRgMaxEntries ? c : kRgMaxEntries;
+}
+
+struct RgShared {
+  int key[kRgMaxSeqs];     // visible keys of each decode row (ranking key)
+  int order[kRgMaxSeqs];   // sequences, most visible keys first
+  int g_s[kRgMaxGroups], g_kvh[kRgMaxGroups], g_lo[kRgMaxGroups], g_q0[kRgMaxGroups];
+  int g_first[kRgMaxGroups + 1];  // first task of each row group; total last
+  int g_done[kRgMaxGroups];       // tasks of the row group whose partial is in the ring
+  int gen[kRgMaxEntries];         // ring entry generations
+  int next_task;
+  int ngroups;
+  int broken;                     // set when a wait ran out: no wait is made after it
+};
+
+__device__ __forceinline__ int rfl(int v) { return __builtin_amdgcn_readfirstlane(v); }
+
+template <int D>
+struct RgWave {
+  const AttnSplitArgs& a;
+  RgShared& sh;
+  char* ring;
+  int lane, g4, G, C, EB, total;
+  int jc, jn, kc, kn;  // task indices of cur and nxt, and their row groups
+  Item cur, nxt;
+  ItemLane<D> curL[1];
+  SplitState<D> st[1];
+  int ct;
+
+  __device__ __forceinline__ int claim() {
+    int v = 0;
+    if (lane == 0) v = __hip_atomic_fetch_add(&sh.next_task, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+    return rfl(v);
+  }
+
+  // Row group of task j: the largest k with g_first[k] <= j (an empty group
+  // shares its g_first with the next one, so the last of equals is taken).
+  __device__ __forceinline__ int group_of(int j) const {
+    int lo = 0, hi = sh.ngroups - 1;
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) >> 1;
+      if (rfl(sh.g_first[mid]) <= j) lo = mid; else hi = mid - 1;
+    }
+    return lo;
+  }
+
+  __device__ __forceinline__ Item task_item(int j, int& k) const {
+    Item it;
+    it.valid = j < total;
+    it.s = 0; it.kvh = 0; it.sigma = 0; it.q0 = 0; it.tq0 = 0; it.nrow_tok = 0; it.k_len = 0; it.p_first = 0;
+    it.tile_begin = 0; it.tile_end = 1; it.last_entry = 0; it.pt_row = a.page_table;
+    k = 0;
+    if (!it.valid) return it;
+    k = group_of(j);
+    const int s = rfl(sh.g_s[k]);
+    fill_item(a, it, s, rfl(sh.g_kvh[k]), rfl(sh.g_lo[k]) + j - rfl(sh.g_first[k]), rfl(sh.g_q0[k]), 1,
+              ldc(a.seq_lens, s), 0, kRowsPerBlock >> a.log2_group);
+    return it;
+  }
+
+  __device__ __forceinline__ void begin_item() {
+    curL[0] = item_lane<D>(a, cur, lane, 0);
+    st[0].init();
+  }
+
+  // Fold the n partials of row group k (entries of tasks g_first[k] ...) in
+  // split order and write its G output rows; then free the entries.
+  __device__ __forceinline__ void merge_group(int k) {
+    constexpr int QPR = D / 4;
+    const int f = rfl(sh.g_first[k]);
+    const int n = rfl(sh.g_first[k + 1]) - f;
+    const int kvh = rfl(sh.g_kvh[k]);
+    const int q0 = rfl(sh.g_q0[k]);
+    for (int qd = lane; qd < G * QPR; qd += 64) {
+      const int r = qd / QPR, d0 = 4 * (qd % QPR);
+      float mstar = -INFINITY;
+      for (int i = 0; i < n; ++i) {
+        const char* ent = ring + ((f + i) % C) * EB;
+        mstar = fmaxf(mstar, reinterpret_cast<const float2*>(ent + G * D * 4)[r].x);
       }
+      float L = 0.f;
+      f32x4 N = {0.f, 0.f, 0.f, 0.f};
+      for (int i = 0; i < n; ++i) {
+        const char* ent = ring + ((f + i) % C) * EB;
+        const float2 ml = reinterpret_cast<const float2*>(ent + G * D * 4)[r];
+        const f32x4 acc = *reinterpret_cast<const f32x4*>(ent + (r * D + d0) * 4);
+        merge_fold(mstar, ml, acc, L, N);
+      }
+      uint16_t* op = a.out + ((int64_t)q0 * a.num_q_heads + (kvh << a.log2_group) + r) * D + d0;
+      *reinterpret_cast<u32x2*>(op) = merge_finish(N, L);
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // the reads above before the entries are reused
+    for (int i = lane; i < n; i += 64)
+      __hip_atomic_store(&sh.gen[(f + i) % C], (f + i) / C + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+  }
+
+  // The current task's partial into its ring entry, and the merge if it was
+  // its row group's last.
+  __device__ __forceinline__ void finish_task() {
+    const int e = jc % C, want = jc / C;
+    for (int spins = 0;; ++spins) {
+      if (rfl(__hip_atomic_load(&sh.gen[e], __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_WORKGROUP)) == want) break;
+      if (rfl(__hip_atomic_load(&sh.broken, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP)) != 0) break;
+      if (spins == kRgSpinLimit) {
+        if (lane == 0) __hip_atomic_store(&sh.broken, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(2);
+    }
+    char* ent = ring + e * EB;
+    const int r = lane & 15;
+    if (r < G) {  // the rows of the block's one token: its G heads
+      if (g4 == 0)
+        reinterpret_cast<float2*>(ent + G * D * 4)[r] = make_float2(st[0].m, st[0].l);
+#pragma unroll
+      for (int n = 0; n < D / 16; ++n)
+        *reinterpret_cast<f32x4*>(ent + (r * D + 16 * n + 4 * g4) * 4) = st[0].acc[n];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");  // every lane's writes before the count
+    int done = 0;
+    if (lane == 0) done = __hip_atomic_fetch_add(&sh.g_done[kc], 1, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_WORKGROUP);
+    done = rfl(done);
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup");
+    if (done == rfl(sh.g_first[kc + 1]) - rfl(sh.g_first[kc]) - 1) merge_group(kc);
+  }
+
+  __device__ __forceinline__ bool step(TileData<D>& Bc, TileData<D>& Bl) {
+    const bool in_cur = ct + 1 < cur.tile_end;
+    const Item& L = in_cur ? cur : nxt;
+    const int lt = in_cur ? ct + 1 : nxt.tile_begin;
+    const int lend = (in_cur || nxt.valid) ? L.tile_end : lt;  // dead load past the last task
+    load_tile(a, L.kvh, L.k_len, lt, lend, tile_pages(L.pt_row, L.last_entry, lt), lane, Bl);
+    __builtin_amdgcn_sched_barrier(0);
+    compute_tile<D, 1>(st, Bc, curL, ct, g4, a.qk_scale_log2);
+    __builtin_amdgcn_sched_barrier(0);
+    if (in_cur) {
+      ++ct;
+      return true;
+    }
+    finish_task();
+    if (!nxt.valid) return false;
+    cur = nxt;
+    jc = jn;
+    kc = kn;
+    begin_item();
+    jn = claim();
+    nxt = task_item(jn, kn);
+    ct = cur.tile_begin;
+    return true;
+  }
+};
+
+template <int D>
+__global__ __launch_bounds__(64 * kRgWaves, 1) void attn_rowgroup_kernel(const AttnSplitArgs a) {
+#if defined(__HIP_DEVICE_COMPILE__)
+  __shared__ RgShared sh;
+  __shared__ __attribute__((aligned(16))) char ring[kRgRingBytes];
+  const int tid = threadIdx.x;
+  constexpr int NT = 64 * kRgWaves;
+  const int B = a.num_seqs;
+  // Visible keys of each decode row, then each sequence's rank (most first).
+  for (int s = tid; s < B; s += NT) {
+    const int q0 = a.qsl[s], q_len = a.qsl[s + 1] - q0, k_len = a.seq_lens[s];
+    int vis = 0;
+    if (q_len == 1 && k_len >= 1) vis = k_len - (a.window > 0 ? max(0, k_len - a.window) : 0);
+    sh.key[s] = vis;
+  }
+  for (int e = tid; e < kRgMaxEntries; e += NT) sh.gen[e] = 0;
+  for (int k = tid; k < kRgMaxGroups; k += NT) sh.g_done[k] = 0;
+  if (tid == 0) {
+    sh.next_task = 0;
+    sh.broken = 0;
+  }
+  __syncthreads();
+  for (int s = tid; s < B; s += NT) {
+    const int v = sh.key[s];
+    int r = 0;
+    for (int t = 0; t < B; ++t) {
+      const int w = sh.key[t];
+      r += (w > v) | ((w == v) & (t < s));
+    }
+    sh.order[r] = s;
+  }
+  __syncthreads();
+  // This workgroup's row groups: position j of the ranked list (sequence
+  // order[j / H_kv], KV head j % H_kv) in a snake over the workgroups.
+  if (tid == 0) {
+    const int W = (int)gridDim.x, g = (int)blockIdx.x, R = B * a.num_kv_heads;
+    int k = 0, first = 0;
+    for (int round = 0; k < kRgMaxGroups; ++round) {
+      const int j = round * W + ((round & 1) ? W - 1 - g : g);
+      if (j >= R) break;
+      const int s = sh.order[j / a.num_kv_heads];
+      const int q0 = a.qsl[s], q_len = a.qsl[s + 1] - q0;
+      const bool ok = q_len == 1 && q0 >= 0 && q0 < a.num_tokens;
+      const SeqSplits sp = ok ? seq_splits(1, a.seq_lens[s], a.window, a.split, a.ns) : SeqSplits{0, 0};
+      sh.g_s[k] = s;
+      sh.g_kvh[k] = j % a.num_kv_heads;
+      sh.g_lo[k] = sp.lo;
+      sh.g_q0[k] = ok ? q0 : -1;
+      sh.g_first[k] = first;
+      first += sp.n;
+      ++k;
+    }
+    sh.g_first[k] = first;
+    sh.ngroups = k;
+  }
+  __syncthreads();
+  const int lane = tid & 63;
+  const int G = 1 << a.log2_group;
+  // A decode row with no visible key (a length of 0, or past the splits the
+  // call was sized for) is written as zeros, as the merge kernel does.
+  if (tid < 64) {
+    for (int k = 0; k < sh.ngroups; ++k) {
+      if (sh.g_first[k + 1] != sh.g_first[k] || sh.g_q0[k] < 0) continue;
+      uint16_t* op = a.out + ((int64_t)sh.g_q0[k] * a.num_q_heads + (sh.g_kvh[k] << a.log2_group)) * D;
+      for (int i = lane; i < G * D / 4; i += 64) *reinterpret_cast<u32x2*>(op + 4 * i) = u32x2{0u, 0u};
     }
   }
-  bf16x4 o;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) o[i] = (__bf16)(N[i] / L + 0.0f);
-  *reinterpret_cast<u32x2*>(op) = __builtin_bit_cast(u32x2, o);
+  RgWave<D> w{a, sh, ring};
+  w.lane = lane;
+  w.g4 = lane >> 4;
+  w.G = G;
+  w.C = rg_entries(D, G);
+  w.EB = rg_entry_bytes(D, G);
+  w.total = rfl(sh.g_first[sh.ngroups]);
+  w.jc = w.claim();
+  w.cur = w.task_item(w.jc, w.kc);
+  if (!w.cur.valid) return;
+  w.begin_item();
+  w.jn = w.claim();
+  w.nxt = w.task_item(w.jn, w.kn);
+  w.ct = w.cur.tile_begin;
+  TileData<D> buf0, buf1;
+  load_tile(a, w.cur.kvh, w.cur.k_len, w.ct, w.cur.tile_end, tile_pages(w.cur.pt_row, w.cur.last_entry, w.ct), lane,
+            buf0);
+  while (w.step(buf0, buf1) && w.step(buf1, buf0)) {
+  }
+#endif
+}
+
+// Workgroups of the row-group kernel resident at once (per device, cached).
+template <int D>
+int resident_rowgroup_groups() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 0;
+  if (cached[dev] > 0) return cached[dev];
+  int cus = 0, per_cu = 0;
+  if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_rowgroup_kernel<D>, 64 * kRgWaves, 0) !=
+      hipSuccess)
+    return 0;
+  cached[dev] = max(1, cus * max(per_cu, 1));
+  return cached[dev];
+}
+
+// Fewest row groups per workgroup for which the row-group mapping is taken
+// (below it the split kernel's finer items balance better).
+constexpr int kRgMinGroupsPerWg = 2;
+
+template <int D>
+bool rowgroup_applies(const AttnSplitArgs& a) {
+  if constexpr (D > 128) {
+    return false;
+  } else {
+    if (a.num_tokens != a.num_seqs || a.num_seqs > kRgMaxSeqs || a.num_seqs < 1) return false;
+    if (a.ns > rg_entries(D, 1 << a.log2_group)) return false;
+    const int64_t groups = resident_rowgroup_groups<D>();
+    if (groups <= 0) return false;
+    const int64_t R = (int64_t)a.num_seqs * a.num_kv_heads;
+    return R <= groups * kRgMaxGroups && R >= groups * kRgMinGroupsPerWg;
+  }
+}
+
+template <int D>
+hipError_t rowgroup_launch(AttnSplitArgs a, hipStream_t stream) {
+  a.qblocks = 1;
+  a.spread = 0;
+  const int groups = resident_rowgroup_groups<D>();
+  if (groups <= 0) return hipErrorInvalidDevice;
+  hipLaunchKernelGGL(attn_rowgroup_kernel<D>, dim3(groups), dim3(64 * kRgWaves), 0, stream, a);
+  return hipGetLastError();
 }
 
 // Workgroups of the persistent split kernel that the current device keeps
@@ -1001,6 +1349,22 @@ hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t s
     case 64: return split_launch<64>(a, stream);
     case 128: return split_launch<128>(a, stream);
     case 256: return split_launch<256>(a, stream);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+bool attn_rowgroup_applies(int head_dim, const AttnSplitArgs& a) {
+  switch (head_dim) {
+    case 64: return rowgroup_applies<64>(a);
+    case 128: return rowgroup_applies<128>(a);
+    default: return false;
+  }
+}
+
+hipError_t launch_attn_rowgroup(int head_dim, const AttnSplitArgs& a, hipStream_t stream) {
+  switch (head_dim) {
+    case 64: return rowgroup_launch<64>(a, stream);
+    case 128: return rowgroup_launch<128>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -38,6 +38,7 @@ struct AttnSplitArgs {
   int32_t* plan;             // [num_seqs + 1]: first work item of each sequence, total last
   int32_t qblocks;           // query-row blocks per work item (set by the launcher)
   int32_t spread;            // 1: consecutive items go to different workgroups (set by the launcher)
+  uint16_t* out;             // bf16 [T][H_q][D]: written directly by the row-group decode mapping
 };
 
 struct AttnMergeArgs {
@@ -55,6 +56,12 @@ struct AttnMergeArgs {
 };
 
 hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t stream);
+// Decode batches (every q_len = 1) with enough (sequence, KV head) row groups
+// to fill the GPU run split and merge in one launch that keeps the partials in
+// LDS and writes only a.out (bitwise the split + merge result).  Returns true
+// when this mapping applies to the arguments (needs the current device).
+bool attn_rowgroup_applies(int head_dim, const AttnSplitArgs& a);
+hipError_t launch_attn_rowgroup(int head_dim, const AttnSplitArgs& a, hipStream_t stream);
 // Query-row blocks per work item the split launch would use for these arguments
 // (needs the current device; 0 on failure).
 int attn_item_blocks(int head_dim, const AttnSplitArgs& a);

@@ -214,6 +214,20 @@ bi_status bi_paged_attention_noalloc(const bi_attn_config* cfg,
 bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                          int32_t max_seq_len, int32_t* blocks);
 
+/* Work mapping of bi_paged_attention (diagnostic): *mapping = 1 when a batch of
+ * this shape runs the row-group mapping — a decode batch (num_tokens ==
+ * num_seqs, so every q_len is 1) with head_dim <= 128, at most 2048 sequences,
+ * at least one (sequence, KV head) row group per compute unit and at most 64,
+ * and few enough splits per row that a row group's partials fit the kernel's
+ * LDS ring (for head_dim 128 and 4 query heads per KV head: up to 59 splits).
+ * There each workgroup computes the splits of whole row groups, keeps their
+ * partials in LDS and merges them itself (Vosti deep-dive blog, §8.1: two
+ * work mappings with the same accumulation order), writing no partials to the
+ * workspace; otherwise (*mapping = 0) the split and merge phases below run.
+ * Both mappings give every row the same bits.  Needs a current device. */
+bi_status bi_paged_attention_mapping(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
+                                    int32_t max_seq_len, int32_t* mapping);
+
 /* The two phases of bi_paged_attention, separately: the split phase writes the
  * workspace partials described above; the merge phase reads them and writes
  * the output.  bi_paged_attention == split then merge on the same stream. */

@@ -123,6 +123,105 @@ def test_headline_pool_every_row_against_the_oracle(headline):
     assert worst <= BF16_TOL, worst
 
 
+# ---------------------------------------------------------------- row-group vs split mapping (cross-kernel)
+
+def _phases(cfg, q, k, v, pt, sl, qsl, msl):
+    """The split and merge phases as separate launches (always the split mapping)."""
+    ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, sl.shape[0], q.shape[0], msl))
+    bi.bi_paged_attention_split(cfg, q, k, v, pt, sl, qsl, msl, ws)
+    return bi.bi_paged_attention_merge(cfg, sl, qsl, q.shape[0], msl, ws)
+
+
+@pytest.mark.parametrize("B,window", [(1, 0), (8, 0), (32, 0), (64, 0), (256, 0), (256, 1000)])
+def test_row_group_mapping_matches_split_and_merge_bitwise(headline, B, window):
+    """Decode batches of the headline pool: bi_paged_attention (the row-group
+    mapping once a batch fills the GPU, the split mapping below) against the
+    split and merge phases launched separately, every row bitwise."""
+    wl = headline
+    cfg = bi.AttnConfig(32, 8, 128, split_size=256, window=window)
+    lens = wl.lengths[:B]
+    q, pt, sl = wl.q[:B], wl.page_table[:B], wl.seq_lens[:B]
+    qsl = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    mapping = bi.bi_paged_attention_mapping(cfg, B, B, max(lens))
+    if B >= 64:
+        assert mapping == 1
+    if B <= 8:
+        assert mapping == 0
+    got = bi.bi_paged_attention(cfg, q, wl.k_cache, wl.v_cache, pt, sl, qsl, max(lens))
+    ref = _phases(cfg, q, wl.k_cache, wl.v_cache, pt, sl, qsl, max(lens))
+    assert first_mismatch(got, ref) is None
+
+
+@pytest.mark.parametrize("Hq,Hk,D,lo,hi", [(4, 2, 64, 17, 3000), (32, 4, 128, 300, 4096), (8, 8, 128, 100, 2000),
+                                           (16, 1, 64, 50, 1500)])
+def test_row_group_mapping_other_head_geometries(Hq, Hk, D, lo, hi):
+    """GQA groups of 2, 8, 1 and 16 and head dim 64: the row-group mapping
+    (where it applies) against the separate phases bitwise, and the oracle on
+    sampled rows."""
+    geom = synth.Geometry(Hq, Hk, D, 16)
+    cfg = bi.AttnConfig(Hq, Hk, D, split_size=256)
+    B = max(1, 2048 // Hk) if Hk < 8 else 300
+    B = min(B, 600)
+    lengths = synth.uniform_ints(B, lo, hi, 3000 + Hq + Hk + D)
+    need = [synth.pages_needed(L, 16) for L in lengths]
+    num_pages = sum(need) + 11
+    perm = synth.permutation(num_pages, 3001)
+    pages, cur = [], 0
+    for n in need:
+        pages.append(perm[cur:cur + n])
+        cur += n
+    k = synth.normal_bf16_device(cfg.k_cache_shape(num_pages), 3002)
+    v = synth.normal_bf16_device(cfg.v_cache_shape(num_pages), 3003)
+    q = synth.normal_bf16_device((B, Hq, D), 3004)
+    pt = page_table_tensor(pages, max(need) + 1).to(DEV)
+    sl = torch.tensor(lengths, dtype=torch.int32, device=DEV)
+    qsl = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    mapping = bi.bi_paged_attention_mapping(cfg, B, B, max(lengths))
+    got = bi.bi_paged_attention(cfg, q, k, v, pt, sl, qsl, max(lengths))
+    ref = _phases(cfg, q, k, v, pt, sl, qsl, max(lengths))
+    assert first_mismatch(got, ref) is None, mapping
+    if Hk in (2, 4, 8) and Hq // Hk <= 8:
+        assert mapping == 1, (Hq, Hk, D)
+    for s in (0, B // 2, B - 1):
+        idx = torch.tensor(pages[s], dtype=torch.long, device=DEV)
+        kk = k.index_select(0, idx).cpu().permute(0, 3, 1, 2, 4).reshape(len(pages[s]), 16, Hk, D)
+        vv = v.index_select(0, idx).cpu().permute(0, 4, 1, 2, 5, 3).reshape(len(pages[s]), 16, Hk, D)
+        ref_o = oracle.attention_ref(synth.to_f64(q[s:s + 1].cpu()), synth.to_f64(kk), synth.to_f64(vv),
+                                     np.arange(len(pages[s]))[None, :], [lengths[s]], [0, 1], Hk, 16)
+        assert float(np.max(np.abs(synth.to_f64(got[s:s + 1].cpu()) - ref_o))) <= BF16_TOL
+
+
+def test_row_group_mapping_lengths_past_max_seq_len():
+    """Lengths past max_seq_len in a batch the row-group mapping takes: rows are
+    truncated at the workspace's splits exactly as the split mapping truncates
+    them (bitwise), and a zero-length row is written as zeros."""
+    geom = synth.Geometry(4, 2, 64, 16)
+    cfg = bi.AttnConfig(4, 2, 64, split_size=32)
+    B = 300
+    lengths = synth.uniform_ints(B, 1, 200, 3100)
+    need = [synth.pages_needed(L, 16) for L in lengths]
+    num_pages = sum(need) + 3
+    perm = synth.permutation(num_pages, 3101)
+    pages, cur = [], 0
+    for n in need:
+        pages.append(perm[cur:cur + n])
+        cur += n
+    k = synth.normal_bf16_device(cfg.k_cache_shape(num_pages), 3102)
+    v = synth.normal_bf16_device(cfg.v_cache_shape(num_pages), 3103)
+    q = synth.normal_bf16_device((B, 4, 64), 3104)
+    pt = page_table_tensor(pages, 13).to(DEV)
+    dev_lens = list(lengths)
+    dev_lens[7] = 0
+    sl = torch.tensor(dev_lens, dtype=torch.int32, device=DEV)
+    qsl = torch.arange(B + 1, dtype=torch.int32, device=DEV)
+    msl = 96                                  # three splits of 32; many rows are longer
+    assert bi.bi_paged_attention_mapping(cfg, B, B, msl) == 1
+    got = bi.bi_paged_attention(cfg, q, k, v, pt, sl, qsl, msl)
+    ref = _phases(cfg, q, k, v, pt, sl, qsl, msl)
+    assert first_mismatch(got, ref) is None
+    assert bool((got[7].float() == 0).all())
+
+
 # ---------------------------------------------------------------- prefill mappings against the oracle
 
 @pytest.mark.parametrize("window", [0, 100])
