@@ -39,6 +39,7 @@ struct AttnSplitArgs {
   int32_t qblocks;           // query-row blocks per work item (set by the launcher)
   int32_t spread;            // 1: consecutive items go to different workgroups (set by the launcher)
   uint16_t* out;             // bf16 [T][H_q][D]: written directly by the row-group decode mapping
+  int32_t rg_static_rounds;  // row-group mapping: rounds of row groups dealt statically (set by the launcher)
 };
 
 struct AttnMergeArgs {

@@ -27,7 +27,10 @@
  *    when it is violated (out-of-range page ids are read as zero pages,
  *    positions past the workspace bound are skipped) but the results of rows
  *    that violate it are unspecified.
- *  - No kernel uses atomics; no kernel communicates across workgroups.
+ *  - No arithmetic result depends on which workgroup or wave computes it, or
+ *    when.  The only atomics hand out work (the row-group mapping of
+ *    bi_paged_attention claims row groups from a counter in the workspace);
+ *    no kernel exchanges data between workgroups.
  */
 #ifndef BI_H_
 #define BI_H_
@@ -161,8 +164,10 @@ bi_status bi_kv_write_paged(const bi_attn_config* cfg, const void* k_new_dev, in
 /*         m = max_j y_j, l = sum_j 2^(y_j - m), y_j = scale*log2(e)*<q,k_j> */
 /*   acc : float  [R][NS][D]  sum_j 2^(y_j - m) v_j, at the first 256-byte   */
 /*         boundary after ml                                                 */
-/*   plan: int32  [num_seqs+1] first work item of each sequence (the split   */
-/*         phase's own schedule), at the first 256-byte boundary after acc   */
+/*   plan: int32  [num_seqs+1] the launch's own schedule (the split phase:  */
+/*         first work item of each sequence; the row-group mapping: the     */
+/*         sequences by visible keys and a claim counter), at the first     */
+/*         256-byte boundary after acc                                       */
 /* Only the splits that meet [lo, p] of a row are written and read.          */
 /* BI_ERR_OUT_OF_RANGE when 16 * H_q * NS * D * 4 >= 2^31 (the partials of    */
 /* one 16-column block are addressed with 32-bit offsets).                   */
@@ -217,9 +222,9 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
 /* Work mapping of bi_paged_attention (diagnostic): *mapping = 1 when a batch of
  * this shape runs the row-group mapping — a decode batch (num_tokens ==
  * num_seqs, so every q_len is 1) with head_dim <= 128, at most 2048 sequences,
- * at least one (sequence, KV head) row group per compute unit and at most 64,
- * and few enough splits per row that a row group's partials fit the kernel's
- * LDS ring (for head_dim 128 and 4 query heads per KV head: up to 59 splits).
+ * at least two (sequence, KV head) row groups per compute unit, and few enough
+ * splits per row that a row group's partials fit the kernel's LDS ring (for
+ * head_dim 128 and 4 query heads per KV head: up to 59 splits).
  * There each workgroup computes the splits of whole row groups, keeps their
  * partials in LDS and merges them itself (Vosti deep-dive blog, §8.1: two
  * work mappings with the same accumulation order), writing no partials to the
