@@ -910,7 +910,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
 // the sequences by visible keys, most first (ties by index), into the
 // workspace plan and zeroes a claim counter after it.  Position r of that
 // order is the row group (sequence order[r / H_kv], KV head r % H_kv).  The
-// row-group kernel runs one workgroup of eight waves per CU (W workgroups).
+// row-group kernel runs one workgroup per CU (W workgroups; eight waves, four
+// at head dim 256).
 // The first rg_static_rounds * W positions are dealt in a snake (round i gives
 // workgroup g position i W + g in even rounds, i W + W - 1 - g in odd ones),
 // so every workgroup starts with a similar total; the rest, the smallest row
@@ -932,7 +933,10 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
 // by a wave that is not waiting: each wait ends.  Each is bounded all the same
 // (a wrong count ends the wait instead of hanging the kernel).
 // ---------------------------------------------------------------------------
-constexpr int kRgWaves = 8;
+// Waves per workgroup: two per SIMD where the split state allows it (head
+// dim <= 128), one at head dim 256.
+template <int D>
+constexpr int rg_waves() { return D <= 128 ? 8 : 4; }
 constexpr int kRgMaxSeqs = 2048;        // sequences the plan launch ranks (in LDS)
 constexpr int kRgRingBytes = 120 * 1024;
 constexpr int kRgMaxEntries = 224;      // ring entries; unmerged row groups < kRgSlots
@@ -1217,12 +1221,12 @@ struct RgWave {
 };
 
 template <int D>
-__global__ __launch_bounds__(64 * kRgWaves, 1) void attn_rowgroup_kernel(const AttnSplitArgs a) {
+__global__ __launch_bounds__(64 * rg_waves<D>(), 1) void attn_rowgroup_kernel(const AttnSplitArgs a) {
 #if defined(__HIP_DEVICE_COMPILE__)
   __shared__ RgShared sh;
   __shared__ __attribute__((aligned(16))) char ring[kRgRingBytes];
   const int tid = threadIdx.x;
-  for (int e = tid; e < kRgMaxEntries; e += 64 * kRgWaves) sh.gen[e] = 0;
+  for (int e = tid; e < kRgMaxEntries; e += 64 * rg_waves<D>()) sh.gen[e] = 0;
   if (tid == 0) {
     sh.lock = 0;
     sh.next_task = 0;
@@ -1265,7 +1269,7 @@ int resident_rowgroup_groups() {
   if (cached[dev] > 0) return cached[dev];
   int cus = 0, per_cu = 0;
   if (hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess) return 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_rowgroup_kernel<D>, 64 * kRgWaves, 0) !=
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, attn_rowgroup_kernel<D>, 64 * rg_waves<D>(), 0) !=
       hipSuccess)
     return 0;
   cached[dev] = max(1, cus * max(per_cu, 1));
@@ -1276,17 +1280,21 @@ int resident_rowgroup_groups() {
 // (below it the split kernel's finer items balance better).
 constexpr int kRgMinGroupsPerWg = 2;
 
+// Most splits a decode row can meet: all ns, or with a window w the splits of
+// w consecutive keys.
+inline int rg_max_row_splits(const AttnSplitArgs& a) {
+  if (a.window <= 0) return a.ns;
+  const int64_t w = (int64_t)a.window + a.split - 2;
+  return (int)std::min<int64_t>(a.ns, w / a.split + 1);
+}
+
 template <int D>
 bool rowgroup_applies(const AttnSplitArgs& a) {
-  if constexpr (D > 128) {
-    return false;
-  } else {
-    if (a.num_tokens != a.num_seqs || a.num_seqs > kRgMaxSeqs || a.num_seqs < 1) return false;
-    if (a.ns > rg_entries(D, 1 << a.log2_group)) return false;
-    const int64_t groups = resident_rowgroup_groups<D>();
-    if (groups <= 0) return false;
-    return (int64_t)a.num_seqs * a.num_kv_heads >= groups * kRgMinGroupsPerWg;
-  }
+  if (a.num_tokens != a.num_seqs || a.num_seqs > kRgMaxSeqs || a.num_seqs < 1) return false;
+  if (rg_max_row_splits(a) > rg_entries(D, 1 << a.log2_group)) return false;
+  const int64_t groups = resident_rowgroup_groups<D>();
+  if (groups <= 0) return false;
+  return (int64_t)a.num_seqs * a.num_kv_heads >= groups * kRgMinGroupsPerWg;
 }
 
 // Rounds of row groups dealt statically: half of the rounds the batch makes,
@@ -1305,7 +1313,7 @@ hipError_t rowgroup_launch(AttnSplitArgs a, hipStream_t stream) {
   hipLaunchKernelGGL(attn_rowgroup_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(attn_rowgroup_kernel<D>, dim3(groups), dim3(64 * kRgWaves), 0, stream, a);
+  hipLaunchKernelGGL(attn_rowgroup_kernel<D>, dim3(groups), dim3(64 * rg_waves<D>()), 0, stream, a);
   return hipGetLastError();
 }
 
@@ -1443,6 +1451,7 @@ bool attn_rowgroup_applies(int head_dim, const AttnSplitArgs& a) {
   switch (head_dim) {
     case 64: return rowgroup_applies<64>(a);
     case 128: return rowgroup_applies<128>(a);
+    case 256: return rowgroup_applies<256>(a);
     default: return false;
   }
 }
@@ -1451,6 +1460,7 @@ hipError_t launch_attn_rowgroup(int head_dim, const AttnSplitArgs& a, hipStream_
   switch (head_dim) {
     case 64: return rowgroup_launch<64>(a, stream);
     case 128: return rowgroup_launch<128>(a, stream);
+    case 256: return rowgroup_launch<256>(a, stream);
     default: return hipErrorInvalidValue;
   }
 }

@@ -221,10 +221,11 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
 
 /* Work mapping of bi_paged_attention (diagnostic): *mapping = 1 when a batch of
  * this shape runs the row-group mapping — a decode batch (num_tokens ==
- * num_seqs, so every q_len is 1) with head_dim <= 128, at most 2048 sequences,
- * at least two (sequence, KV head) row groups per compute unit, and few enough
- * splits per row that a row group's partials fit the kernel's LDS ring (for
- * head_dim 128 and 4 query heads per KV head: up to 59 splits).
+ * num_seqs, so every q_len is 1) of at most 2048 sequences with at least two
+ * (sequence, KV head) row groups per compute unit, where a row meets few
+ * enough splits (all ceil(max_seq_len / S), or with a window those of w keys)
+ * that a row group's partials fit the kernel's LDS ring (up to 59 splits for
+ * head_dim 128 with 4 query heads per KV head, or head_dim 256 with 2).
  * There each workgroup computes the splits of whole row groups, keeps their
  * partials in LDS and merges them itself (Vosti deep-dive blog, §8.1: two
  * work mappings with the same accumulation order), writing no partials to the

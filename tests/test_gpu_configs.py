@@ -152,16 +152,18 @@ def test_row_group_mapping_matches_split_and_merge_bitwise(headline, B, window):
     assert first_mismatch(got, ref) is None
 
 
-@pytest.mark.parametrize("Hq,Hk,D,lo,hi", [(4, 2, 64, 17, 3000), (32, 4, 128, 300, 4096), (8, 8, 128, 100, 2000),
-                                           (16, 1, 64, 50, 1500)])
-def test_row_group_mapping_other_head_geometries(Hq, Hk, D, lo, hi):
-    """GQA groups of 2, 8, 1 and 16 and head dim 64: the row-group mapping
-    (where it applies) against the separate phases bitwise, and the oracle on
+@pytest.mark.parametrize("Hq,Hk,D,lo,hi,window", [(4, 2, 64, 17, 3000, 0), (32, 4, 128, 300, 4096, 0),
+                                                  (8, 8, 128, 100, 2000, 0), (16, 1, 64, 50, 1500, 0),
+                                                  (8, 4, 256, 512, 4096, 0), (8, 4, 256, 100, 20000, 1024)])
+def test_row_group_mapping_other_head_geometries(Hq, Hk, D, lo, hi, window):
+    """GQA groups of 2, 8, 1 and 16, head dims 64 and 256 (the Gemma-shaped
+    layers: global, and local with a 1024 window over contexts up to 20000,
+    more splits than the ring holds but a window that meets at most five): the
+    row-group mapping against the separate phases bitwise, and the oracle on
     sampled rows."""
-    geom = synth.Geometry(Hq, Hk, D, 16)
-    cfg = bi.AttnConfig(Hq, Hk, D, split_size=256)
+    cfg = bi.AttnConfig(Hq, Hk, D, split_size=256, window=window)
     B = max(1, 2048 // Hk) if Hk < 8 else 300
-    B = min(B, 600)
+    B = min(B, 600 if hi <= 4096 else 256)
     lengths = synth.uniform_ints(B, lo, hi, 3000 + Hq + Hk + D)
     need = [synth.pages_needed(L, 16) for L in lengths]
     num_pages = sum(need) + 11
@@ -187,7 +189,7 @@ def test_row_group_mapping_other_head_geometries(Hq, Hk, D, lo, hi):
         kk = k.index_select(0, idx).cpu().permute(0, 3, 1, 2, 4).reshape(len(pages[s]), 16, Hk, D)
         vv = v.index_select(0, idx).cpu().permute(0, 4, 1, 2, 5, 3).reshape(len(pages[s]), 16, Hk, D)
         ref_o = oracle.attention_ref(synth.to_f64(q[s:s + 1].cpu()), synth.to_f64(kk), synth.to_f64(vv),
-                                     np.arange(len(pages[s]))[None, :], [lengths[s]], [0, 1], Hk, 16)
+                                     np.arange(len(pages[s]))[None, :], [lengths[s]], [0, 1], Hk, 16, window=window)
         assert float(np.max(np.abs(synth.to_f64(got[s:s + 1].cpu()) - ref_o))) <= BF16_TOL
 
 
