@@ -45,7 +45,7 @@ PEAK_HBM_GBPS = 8000.0
 HQ, HKV, D, P, S = 32, 8, 128, 16, 256
 HIDDEN = 4096
 QKV_N = (HQ + 2 * HKV) * D
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_split_traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_b256_traffic.json")
 KERNEL_SOURCES = ["deterministic_paged_attention_amd/csrc/attention.hip"]
 
 
@@ -58,8 +58,9 @@ def kernel_source_hash() -> str:
 
 
 def measured_traffic(batch: int):
-    """HBM bytes per split launch from committed rocprofv3 counter runs, if they
-    were taken on the current kernel source; else None."""
+    """HBM bytes per attention launch (the row-group kernel at batch 256) from
+    committed rocprofv3 counter runs, if they were taken on the current kernel
+    source; else None."""
     try:
         with open(TRAFFIC_FILE) as f:
             t = json.load(f)
