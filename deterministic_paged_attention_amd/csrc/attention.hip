@@ -204,6 +204,15 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // order, it would alone.  A row with no visible key in the tile keeps
 // (m, l, acc) bit-for-bit (select, not update).
 //
+// KEEP = false drops the keep-state selects: a row with no visible key in the
+// tile then has m_new == m, alpha == 1 (or 0 on a still-empty row) and P == 0,
+// so m and l come out bit-for-bit the same and acc gains only +-0 terms, which
+// can change nothing but the sign of an exact-zero accumulator; the merge adds
+// such an accumulator into a sum that starts at +0 and stores -0 as +0, so every
+// output bit is the same either way.  (Which form a kernel uses is a matter of
+// its register allocation: without them the one-block decode kernel spills to
+// the accumulator file, with them the shared-tile kernel is slower.)
+//
 // Two wave-uniform shortcuts leave every value bit-for-bit as computed in
 // full: the key masks are applied only when some row of the wave does not see
 // all 32 keys of the tile (a masked score is -inf, an unmasked one passes
@@ -212,7 +221,7 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // that is still +0, so acc * alpha == acc).  Rescaling in place before the PV
 // product equals scaling its input: a row without a visible key has
 // m_new == m and keeps its accumulator either way.
-template <int D, int QB>
+template <int D, int QB, bool KEEP = true>
 __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const TileData<D>& t,
                                              const ItemLane<D> (&L)[QB], int tile, int g4, float qk_scale_log2) {
   constexpr int NSTEP = D / 32;
@@ -305,14 +314,14 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
 #pragma unroll
     for (int b = 0; b < QB; ++b) {
       const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, vv), pfrag[b], st[b].acc[n]);
-      st[b].acc[n] = live[b] ? res : st[b].acc[n];
+      st[b].acc[n] = (!KEEP || live[b]) ? res : st[b].acc[n];
     }
   }
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
     const float l_new = __builtin_fmaf(alpha[b], st[b].l, rs[b]);
-    st[b].m = live[b] ? m_new[b] : st[b].m;
-    st[b].l = live[b] ? l_new : st[b].l;
+    st[b].m = (!KEEP || live[b]) ? m_new[b] : st[b].m;
+    st[b].l = (!KEEP || live[b]) ? l_new : st[b].l;
   }
 }
 
@@ -393,11 +402,33 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) 
 // plan to the workspace first.
 constexpr int kLdsPlanSeqs = 2048;
 
-// Plan entry i, from the workgroup's LDS copy or from the workspace; both are
+// Up to this many sequences the shared-tile kernel computes plan entries from
+// the sequence table when it needs them (a scalar loop) instead of reading a
+// plan written by a separate launch.
+constexpr int kScanPlanSeqs = 16;
+
+// Work items of sequence s: query-row groups x KV heads x splits (the count
+// plan_scan sums).
+__device__ __forceinline__ int seq_items(const AttnSplitArgs& a, int s) {
+  const int q0 = ldc(a.qsl, s);
+  const int q_len = ldc(a.qsl, s + 1) - q0;
+  const SeqSplits sp = seq_splits(q_len, ldc(a.seq_lens, s), a.window, a.split, a.ns);
+  const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
+  return sp.n > 0 ? ((q_len + tq - 1) / tq) * a.num_kv_heads * sp.n : 0;
+}
+
+// Plan entry i (the first item of sequence i; the total at i = num_seqs), from
+// the workgroup's LDS copy, from the workspace, or computed on demand; all are
 // wave-uniform.
 struct PlanView {
-  const int* lds;  // nullptr: the workspace copy a.plan
+  const int* lds;  // nullptr: the workspace copy a.plan (or computed, with scan)
+  int scan;        // 1: entries computed from the sequence table (few sequences)
   __device__ __forceinline__ int at(const AttnSplitArgs& a, int i) const {
+    if (scan) {
+      int c = 0;
+      for (int s = 0; s < i; ++s) c += seq_items(a, s);
+      return c;
+    }
     return lds ? __builtin_amdgcn_readfirstlane(lds[i]) : ldc(a.plan, i);
   }
 };
@@ -588,6 +619,7 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
   __shared__ int carry_sh;
   SplitWave<D, QB> w{a};
   w.pv.lds = nullptr;
+  w.pv.scan = 0;
   if (a.num_seqs <= kLdsPlanSeqs) {
     plan_scan<64 * kSplitWaves>(a, wave_tot, &carry_sh, [&](int i, int v) { plan_s[i] = v; });
     __syncthreads();
@@ -763,11 +795,13 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
   __shared__ __attribute__((aligned(1024))) char ring[S::R * S::TILE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // The plan comes from the workspace (scalar loads): an LDS copy would be read
+  // The plan comes from the workspace (scalar loads), or for a few sequences
+  // is computed from the sequence table on demand: an LDS copy would be read
   // by ordinary LDS loads, which the compiler must order after every copy to
   // LDS still in flight.
   PlanView pv;
   pv.lds = nullptr;
+  pv.scan = a.num_seqs <= kScanPlanSeqs ? 1 : 0;
   const int total = pv.at(a, a.num_seqs);
   const int G = (int)gridDim.x;
   TileCursor cc, lc;
@@ -795,7 +829,7 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
     __builtin_amdgcn_s_barrier();  // A: tile i is in slot `slot`
     shared_read_tile<D>(a, cc, ring_addr + slot * S::TILE, lane, td);
     __builtin_amdgcn_s_barrier();  // B: every wave has read slot `slot`
-    compute_tile<D, 2>(st, td, L, cc.t, lane >> 4, a.qk_scale_log2);
+    compute_tile<D, 2, false>(st, td, L, cc.t, lane >> 4, a.qk_scale_log2);
     const Item done = cc.it;
     if (cc.advance(a, pv, G, total)) {
 #pragma unroll
@@ -1411,9 +1445,11 @@ hipError_t shared_launch(AttnSplitArgs a, hipStream_t stream) {
   a.spread = 0;
   const int groups = resident_shared_groups<D>();
   if (groups <= 0) return hipErrorInvalidDevice;
-  hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (a.num_seqs > kScanPlanSeqs) {
+    hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
   hipLaunchKernelGGL(attn_split_shared_kernel<D>, dim3(groups), dim3(64 * kSharedWaves), 0, stream, a);
   return hipGetLastError();
 }
