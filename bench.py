@@ -629,7 +629,7 @@ def bench_prefill(args):
     stride = max(len(t) for t in tables)
     flush = mall_flusher()
     rows = []
-    for budget in (16, 128, 512, 0):
+    for budget in [int(b) for b in args.budgets.split(",")]:
         steps = prefill_schedule(unique, budget)
         meta = []
         max_ws = 0
@@ -674,7 +674,7 @@ def bench_prefill(args):
         print(json.dumps({"progress": rows[-1]}), file=sys.stderr, flush=True)
         del graph, meta, outs, ws
         torch.cuda.empty_cache()
-    head = [r for r in rows if r["budget"] == 512][0]
+    head = ([r for r in rows if r["budget"] == 512] or rows)[0]
     print(json.dumps({
         "metric": "batch-invariant chunked prefill attention tokens/s", "value": head["tokens_per_s"],
         "unit": "tokens/s", "n_gpus": 1, "steps": len(rows), "warmup": 1, "ms_per_step": head["ms"]["median"],
@@ -897,6 +897,8 @@ def main():
     ap.add_argument("--user-delay", type=float, default=0.5)
     ap.add_argument("--prefill-budget", type=int, default=2048)
     ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--budgets", default="16,128,512,0",
+                    help="prefill workload: chunk budgets to run (0 = token by token)")
     ap.add_argument("--seed", type=int, default=2000)
     ap.add_argument("--cpu-sample", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")

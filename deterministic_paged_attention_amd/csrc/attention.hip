@@ -659,11 +659,12 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
 // tile) leaves room for two waves per SIMD.
 //
 // Per step i (all four waves walk the same stream of tiles):
-//   issue this wave's chunks of tile i + R - 1 into slot (i - 1) % R, wait
-//   for this wave's chunks of tile i;  barrier A;  read slot i % R into
-//   registers;  barrier B;  compute tile i for the wave's two blocks (and
-//   write their partials at an item's last tile).
-// Slot (i - 1) % R was read by every wave before barrier B of step i - 1.
+//   issue this wave's chunks of tile i + PD into slot (i + PD) % R, wait for
+//   this wave's chunks of tile i;  barrier;  read slot i % R into registers;
+//   compute tile i for the wave's two blocks (and write their partials at an
+//   item's last tile).
+// Slot (i + PD) % R last held tile i + PD - R <= i - 2, which every wave read
+// before it reached the barrier of step i - 1: one barrier per step suffices.
 // Each wave issues the same number of copies every step (tiles past the end
 // of the stream copy nothing, through an empty resource), so its wait count
 // is fixed; loads and stores it issues besides only make that wait stronger.
@@ -676,7 +677,9 @@ struct SharedShape {
   static constexpr int KCH = D / 32;       // 1 KiB chunks per K (or V) page of one KV head
   static constexpr int NCH = 4 * KCH;      // chunks per tile: K page 0, K page 1, V page 0, V page 1
   static constexpr int TILE = NCH * 1024;  // bytes per ring slot
-  static constexpr int R = 3;              // ring slots
+  static constexpr int R = 4;              // ring slots
+  static constexpr int PD = 2;             // tiles loading ahead of the one computed
+  static_assert(R - PD >= 2, "a refilled slot was read two steps earlier: one barrier per step orders it");
   static constexpr int CPW = NCH / kSharedWaves;  // chunks per wave per tile
   static_assert(NCH % kSharedWaves == 0, "chunks split evenly over the waves");
 };
@@ -809,7 +812,7 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
   if (!cc.it.valid) return;  // the whole workgroup: the item index depends on blockIdx only
   lc = cc;
   const uint32_t ring_addr = (uint32_t)(uintptr_t)(lds_void_t*)ring;
-  for (int p = 0; p < S::R - 1; ++p) {  // tiles 0 .. R - 2 into slots 0 .. R - 2
+  for (int p = 0; p < S::PD; ++p) {  // tiles 0 .. PD - 1 into slots 0 .. PD - 1
     shared_issue<D>(a, lc, ring, p, wave, lane);
     lc.advance(a, pv, G, total);
   }
@@ -823,12 +826,11 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
   TileData<D> td;
   int slot = 0;  // ring slot of step i (i % R)
   for (;;) {
-    shared_issue<D>(a, lc, ring, slot == 0 ? S::R - 1 : slot - 1, wave, lane);
-    shared_wait_vm<(S::R - 1) * S::CPW>();  // the chunks of the R - 1 later tiles may still fly
+    shared_issue<D>(a, lc, ring, (slot + S::PD) % S::R, wave, lane);
+    shared_wait_vm<S::PD * S::CPW>();  // the chunks of the PD later tiles may still fly
     lc.advance(a, pv, G, total);
-    __builtin_amdgcn_s_barrier();  // A: tile i is in slot `slot`
+    __builtin_amdgcn_s_barrier();  // tile i is in slot `slot`
     shared_read_tile<D>(a, cc, ring_addr + slot * S::TILE, lane, td);
-    __builtin_amdgcn_s_barrier();  // B: every wave has read slot `slot`
     compute_tile<D, 2, false>(st, td, L, cc.t, lane >> 4, a.qk_scale_log2);
     const Item done = cc.it;
     if (cc.advance(a, pv, G, total)) {

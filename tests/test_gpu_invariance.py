@@ -174,11 +174,11 @@ def test_shared_items_head_dim_64_agree_with_one_block_items():
     rows token by token, bitwise."""
     geom = synth.Geometry(4, 2, 64, 16)
     cfg = bi.AttnConfig(4, 2, 64, split_size=256)
-    reqs = _pool(geom, 16, seed=71, lo=560, hi=640)
+    reqs = _pool(geom, 48, seed=71, lo=560, hi=640)
     T = sum(r.length for r in reqs.values())
-    assert bi.bi_paged_attention_item_blocks(cfg, 16, T, 640) == 8
+    assert bi.bi_paged_attention_item_blocks(cfg, 48, T, 640) == 8
     one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=11)
-    sample = {i: reqs[i] for i in (0, 9, 15)}
+    sample = {i: reqs[i] for i in (0, 9, 47)}
     by_token = _run_schedule(cfg, sample, _chunked(sample, 1), page_seed=12)
     assert _assert_same(one_shot, by_token, "token by token vs one shot") == sum(r.length for r in sample.values())
 
