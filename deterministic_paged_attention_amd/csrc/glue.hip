@@ -128,7 +128,11 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_
   if (h >= num_q_heads + num_kv_heads) {  // v row: copy into the cache
     if (base < 0) return;
     const int o = slots[t] & 15;
-    for (int d = lane; d < head_dim; d += 64) v_cache[base + v_elem(d, o)] = x[d];
+    // head dims d (e = 0) and d + 16 (e = 1) of one (np, r) are adjacent: one 4-byte store
+    for (int j = lane; j < head_dim / 2; j += 64) {
+      const int d = 32 * (j >> 4) + (j & 15);
+      *reinterpret_cast<uint32_t*>(v_cache + base + v_elem(d, o)) = (uint32_t)x[d] | ((uint32_t)x[d + 16] << 16);
+    }
     return;
   }
   const int s = find_token_seq(qsl, num_seqs, num_tokens, t);
@@ -137,12 +141,16 @@ __global__ __launch_bounds__(256) void qk_norm_rope_kernel(uint16_t* qkv, int64_
   norm_rope_row(x, h < num_q_heads ? gamma_q : gamma_k, head_dim, p, eps, log2_theta, lane, z);
   if (base >= 0) {  // k row: the rotated values into the cache
     const int o = slots[t] & 15, half = head_dim / 2;
+    // head dims i and i + 1 (i even) are adjacent in a K chunk: the odd lane's
+    // values travel to the even lane, which makes one 4-byte store of each pair
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int i = lane + 64 * j;
-      if (i < half) {
-        k_cache[base + k_elem(i, o)] = z[j];
-        k_cache[base + k_elem(i + half, o)] = z[2 + j];
+      const uint32_t lo_next = (uint32_t)__shfl_down((int)z[j], 1);
+      const uint32_t hi_next = (uint32_t)__shfl_down((int)z[2 + j], 1);
+      if (i < half && (lane & 1) == 0) {
+        *reinterpret_cast<uint32_t*>(k_cache + base + k_elem(i, o)) = (uint32_t)z[j] | (lo_next << 16);
+        *reinterpret_cast<uint32_t*>(k_cache + base + k_elem(i + half, o)) = (uint32_t)z[2 + j] | (hi_next << 16);
       }
     }
   }

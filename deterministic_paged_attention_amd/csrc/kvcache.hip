@@ -72,38 +72,47 @@ struct SlotSource {
   }
 };
 
-// One thread per (token, KV head, 8-element head-dim chunk c).
-// K cache [page][h][D/8][16][8]: the chunk is one 16-byte store.
+// One thread per (token, KV head, pair of 8-element head-dim chunks c0, c0 + 2):
+// c0 = 4k or 4k + 1, so the two chunks hold head dims d and d + 16 with the
+// same (np, r) of the V layout.
+// K cache [page][h][D/8][16][8]: each chunk is one 16-byte store.
 // V cache [page][h][D/32][16][16][2] (head-dim d = 32*np + 16*e + r, token o at
-// ((np*16 + r)*16 + o)*2 + e): eight 2-byte stores.
+// ((np*16 + r)*16 + o)*2 + e): the e = 0 and e = 1 values of one (np, r) are
+// adjacent, so the pair of chunks is eight 4-byte stores.
 template <int D>
 __global__ __launch_bounds__(256) void kv_write_kernel(int num_kv_heads, const uint16_t* k_new, int64_t k_stride,
                                                        const uint16_t* v_new, int64_t v_stride,
                                                        const SlotSource slots, int32_t num_tokens,
                                                        uint16_t* k_cache, uint16_t* v_cache, int32_t num_pages) {
-  constexpr int NC = D / 8;
+  constexpr int NP = D / 16;  // chunk pairs per head
   const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t total = (int64_t)num_tokens * num_kv_heads * NC;
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * NP;
   if (gid >= total) return;
-  const int c = (int)(gid % NC);
-  const int h = (int)((gid / NC) % num_kv_heads);
-  const int t = (int)(gid / ((int64_t)NC * num_kv_heads));
+  const int q = (int)(gid % NP);
+  const int h = (int)((gid / NP) % num_kv_heads);
+  const int t = (int)(gid / ((int64_t)NP * num_kv_heads));
   const int slot = slots.at(t, num_pages);
   if (slot < 0) return;
   const int pg = slot >> 4;
   const int o = slot & 15;
   if (pg >= num_pages) return;
+  const int c0 = 4 * (q >> 1) + (q & 1), c1 = c0 + 2;
   const int64_t head_base = ((int64_t)pg * num_kv_heads + h) * (D * 16);
-  const u32x4 kv = *reinterpret_cast<const u32x4*>(k_new + (int64_t)t * k_stride + h * D + 8 * c);
-  *reinterpret_cast<u32x4*>(k_cache + head_base + (c * 16 + o) * 8) = kv;
-  const u32x4 vv = *reinterpret_cast<const u32x4*>(v_new + (int64_t)t * v_stride + h * D + 8 * c);
-  // d = 8c + i: np = c / 4, e = (c / 2) & 1, r = 8 * (c & 1) + i.
-  const int np = c >> 2, ev = (c >> 1) & 1, r0 = 8 * (c & 1);
-  uint16_t* vd = v_cache + head_base + ((int64_t)(np * 16 + r0) * 16 + o) * 2 + ev;
+  const uint16_t* kr = k_new + (int64_t)t * k_stride + h * D;
+  const uint16_t* vr = v_new + (int64_t)t * v_stride + h * D;
+  const u32x4 k0 = *reinterpret_cast<const u32x4*>(kr + 8 * c0);
+  const u32x4 k1 = *reinterpret_cast<const u32x4*>(kr + 8 * c1);
+  *reinterpret_cast<u32x4*>(k_cache + head_base + (c0 * 16 + o) * 8) = k0;
+  *reinterpret_cast<u32x4*>(k_cache + head_base + (c1 * 16 + o) * 8) = k1;
+  const u32x4 v0 = *reinterpret_cast<const u32x4*>(vr + 8 * c0);
+  const u32x4 v1 = *reinterpret_cast<const u32x4*>(vr + 8 * c1);
+  // d = 8 c0 + i: np = c0 / 4, r = 8 (c0 & 1) + i; its e = 1 partner d + 16 is element i of chunk c1.
+  const int np = c0 >> 2, r0 = 8 * (c0 & 1);
+  uint32_t* vd = reinterpret_cast<uint32_t*>(v_cache + head_base + ((int64_t)(np * 16 + r0) * 16 + o) * 2);
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    vd[(2 * i) * 32] = (uint16_t)(vv[i] & 0xffffu);
-    vd[(2 * i + 1) * 32] = (uint16_t)(vv[i] >> 16);
+    vd[(2 * i) * 16] = (v0[i] & 0xffffu) | (v1[i] << 16);
+    vd[(2 * i + 1) * 16] = (v0[i] >> 16) | (v1[i] & 0xffff0000u);
   }
 }
 
@@ -111,7 +120,7 @@ template <int D>
 hipError_t kv_write_launch(int num_kv_heads, const uint16_t* k_new, int64_t k_stride, const uint16_t* v_new,
                            int64_t v_stride, const SlotSource& slots, int32_t num_tokens, uint16_t* k_cache,
                            uint16_t* v_cache, int32_t num_pages, hipStream_t stream) {
-  const int64_t total = (int64_t)num_tokens * num_kv_heads * (D / 8);
+  const int64_t total = (int64_t)num_tokens * num_kv_heads * (D / 16);
   if (total == 0) return hipSuccess;
   hipLaunchKernelGGL(kv_write_kernel<D>, dim3((unsigned)((total + 255) / 256)), dim3(256), 0, stream,
                      num_kv_heads, k_new, k_stride, v_new, v_stride, slots, num_tokens, k_cache, v_cache,
