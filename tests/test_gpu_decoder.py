@@ -247,6 +247,74 @@ def test_logits_bitwise_across_batch_chunking_layout_and_prefix_reuse(decoder):
         assert first_mismatch(alone[k], batched[k]) is None and first_mismatch(alone[k], chunked[k]) is None, k
 
 
+def test_decode_step_logits_bitwise_at_batch_256(decoder):
+    """The decode step at batch 256 over synthetic caches (contexts U{64..600}
+    plus one of 32767 tokens), against the same sequences in batches of 64 in
+    another order on relocated pages with wider tables, alone, and as a batch
+    of 255 without the long one: every logits row bitwise.  At 256 the local
+    layers take the row-group attention mapping and the global ones (128 splits
+    per row) the split mapping; at 255 every layer takes the row-group mapping;
+    below, the split mapping."""
+    s = SHAPE
+    B = 256
+    ctx = synth.uniform_ints(B, 64, 600, 5100)
+    ctx[7] = 32767
+    k_lens = [L + 1 for L in ctx]
+    need = [synth.pages_needed(L, 16) for L in k_lens]
+    num_pages = sum(need) + 8
+    perm = synth.permutation(num_pages, 5101)
+    tables, cur = [], 0
+    for n in need:
+        tables.append(perm[cur:cur + n])
+        cur += n
+    caches = decoder.new_caches(num_pages)
+    g = torch.Generator(device=DEV)
+    g.manual_seed(5102)
+    for k, v in caches:
+        k.normal_(generator=g)
+        v.normal_(generator=g)
+    ids = synth.uniform_ints(B, 0, s.vocab - 1, 5103)
+
+    def run(group, cch, tabs, stride_extra=0, fill=-1):
+        pt = page_table_tensor([tabs[i] for i in group], max(len(tabs[i]) for i in group) + stride_extra, fill).to(DEV)
+        sl = torch.tensor([k_lens[i] for i in group], dtype=torch.int32, device=DEV)
+        qsl = torch.arange(len(group) + 1, dtype=torch.int32, device=DEV)
+        ii = torch.tensor([ids[i] for i in group], dtype=torch.int32, device=DEV)
+        logits = decoder.step(ii, cch, pt, sl, qsl, max(k_lens[i] for i in group))
+        return {i: logits[j] for j, i in enumerate(group)}
+
+    full = run(list(range(B)), caches, tables)
+    c_local = decoder.cfg(0)
+    assert bi.bi_paged_attention_mapping(c_local, B, B, max(k_lens)) == 1
+    assert bi.bi_paged_attention_mapping(decoder.cfg(5), B, B, max(k_lens)) == 0
+    # batch of 255 (no long context): row-group mapping in every layer
+    rest = [i for i in range(B) if i != 7]
+    assert bi.bi_paged_attention_mapping(decoder.cfg(5), 255, 255, max(k_lens[i] for i in rest)) == 1
+    got = run(rest[::-1], caches, tables)
+    for i in rest:
+        assert first_mismatch(got[i], full[i]) is None, ("batch 255", i)
+    # batches of 64 in another order, pages relocated, tables wider than needed
+    pos = synth.permutation(num_pages, 5104)
+    idx = torch.tensor(pos, dtype=torch.long, device=DEV)
+    moved = []
+    for k, v in caches:
+        k2, v2 = torch.empty_like(k), torch.empty_like(v)
+        k2.index_copy_(0, idx, k)
+        v2.index_copy_(0, idx, v)
+        moved.append((k2, v2))
+    tables2 = [[pos[p] for p in t] for t in tables]
+    order = synth.permutation(B, 5105)
+    for b0 in range(0, B, 64):
+        got = run(order[b0:b0 + 64], moved, tables2, stride_extra=3, fill=77777)
+        for i, row in got.items():
+            assert first_mismatch(row, full[i]) is None, ("batches of 64", i)
+    del moved
+    # alone: the long context, the shortest and two others
+    for i in (7, min(range(B), key=lambda j: ctx[j]), 100, 255):
+        got = run([i], caches, tables, stride_extra=1)
+        assert first_mismatch(got[i], full[i]) is None, ("alone", i)
+
+
 @pytest.mark.parametrize("Hq,Hk,D", [(8, 4, 256), (32, 8, 128), (4, 2, 64)])
 def test_qk_norm_rope_kv_write_is_the_two_launches(Hq, Hk, D):
     """The fused q/k norm + RoPE + cache write leaves qkv and both caches bitwise
