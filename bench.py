@@ -440,7 +440,7 @@ def bench_decode_sweep(args):
     reps = max(args.steps, 20)
     props = torch.cuda.get_device_properties(0)
     rows = []
-    for B in (1, 8, 64, 256):
+    for B in [int(b) for b in args.batches.split(",")]:
         wl = build_decode_workload(HQ, HKV, D, batch=B, seed=args.seed, lengths=pool[:B])
         ws = bi.alloc_workspace(bi.bi_paged_attention_workspace_size(cfg, B, B, wl.max_seq_len))
         out = torch.empty((B, HQ, D), dtype=torch.bfloat16, device="cuda")
@@ -496,7 +496,7 @@ def bench_gemm(args):
     cpu = None
     for N, odt in ((14336, torch.bfloat16), (128256, torch.float32)):
         W = synth.normal_bf16_device((N, K), args.seed + 40 + N % 7, std=0.02)
-        for M in (1, 7, 64, 256, 1024):
+        for M in [int(m) for m in args.ms.split(",")]:
             x = synth.normal_bf16_device((M, K), args.seed + 50 + M)
             g = synth.normal_bf16_device((K,), args.seed + 49, std=0.1, mean=1.0)
             xn = torch.empty_like(x)
@@ -509,7 +509,7 @@ def bench_gemm(args):
             t_gemm = pct(rep_times_ms(gem, reps, flush))
             per_k = {}
             for ks in (1, 2, 4, 8, 16):
-                if K % (32 * ks) or M * N * 4 * ks > (2 << 30):
+                if K % (32 * ks) or M * N * 4 * ks > (2 << 30) or (args.no_splitk and ks > 1):
                     continue
                 ws = torch.empty(M * N * ks, dtype=torch.float32, device="cuda")
                 c2 = torch.empty_like(c)
@@ -545,7 +545,7 @@ def bench_gemm(args):
         r["mfma_frac_of_measured_peak"] = round(r["gemm_tflops"] / mfma_ref["tflops"], 4)
     if not args.no_cpu_baseline:
         cpu = gemm_cpu_baseline(w_host, args.seed)
-    head = [r for r in rows if r["N"] == 14336 and r["M"] == 256][0]
+    head = ([r for r in rows if r["N"] == 14336 and r["M"] == 256] or rows)[0]
     print(json.dumps({
         "metric": "batch-invariant RMSNorm + GEMM: GEMM fraction of roofline", "value": head["frac_of_roofline"],
         "unit": "fraction of min(bf16 MFMA peak, HBM) roofline", "n_gpus": 1, "steps": reps, "warmup": 1,
@@ -897,6 +897,8 @@ def main():
     ap.add_argument("--user-delay", type=float, default=0.5)
     ap.add_argument("--prefill-budget", type=int, default=2048)
     ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--batches", default="1,8,64,256", help="decode-sweep workload: batch sizes to run")
+    ap.add_argument("--ms", default="1,7,64,256,1024", help="gemm workload: token counts M to run")
     ap.add_argument("--budgets", default="16,128,512,0",
                     help="prefill workload: chunk budgets to run (0 = token by token)")
     ap.add_argument("--seed", type=int, default=2000)
