@@ -244,8 +244,8 @@ def bench_decode(args):
         step()
     torch.cuda.synchronize()
 
-    # Timed region: K steps; the only events inside bracket the split kernel
-    # (its launch duration feeds the roofline).
+    # Timed region: K steps; the only events inside bracket the attention
+    # launch (its duration feeds the roofline).
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(2)] for _ in range(args.steps)]
     t_start = torch.cuda.Event(enable_timing=True)
     t_end = torch.cuda.Event(enable_timing=True)
