@@ -41,6 +41,8 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 METRIC = "batch-invariant paged-attn decode HBM GB/s (% peak) + overhead vs split-K"
+# bi_paged_attention_mapping's answer, by value.
+MAPPING_NAMES = {0: "split + merge", 1: "row-group"}
 PEAK_HBM_GBPS = 8000.0
 HQ, HKV, D, P, S = 32, 8, 128, 16, 256
 HIDDEN = 4096
@@ -357,7 +359,7 @@ def bench_decode(args):
                      "kernel": "attn_rowgroup_kernel<128>" if mapping == 1 else
                                "attn_split_kernel<128, 1> + attn_merge_kernel<128>",
                      "algorithmic_bytes_per_launch": sb,
-                     "avg_launch_us": round(attn_launch_us, 2), "mapping": "row-group" if mapping == 1 else "split + merge",
+                     "avg_launch_us": round(attn_launch_us, 2), "mapping": MAPPING_NAMES[mapping],
                      "measured_stream_read_gbps": read_ref["gbps"],
                      "frac_of_measured_stream_read": round(achieved / read_ref["gbps"], 4)},
         "cpu_baseline": cpu,
@@ -465,7 +467,7 @@ def bench_decode_sweep(args):
         nbytes = split_bytes(wl.lengths) + B * HQ * D * 2
         gbps = nbytes / (t_inv["median"] * 1e-3) / 1e9
         mapping = bi.bi_paged_attention_mapping(cfg, B, B, wl.max_seq_len)
-        rows.append({"batch": B, "mapping": "row-group" if mapping == 1 else "split + merge",
+        rows.append({"batch": B, "mapping": MAPPING_NAMES[mapping],
                      "algorithmic_bytes": nbytes, "invariant_ms": {k: round(v, 4) for k, v in t_inv.items()},
                      "gbps": round(gbps, 1), "frac_of_peak": round(gbps / PEAK_HBM_GBPS, 4),
                      "splitk_ms": round(per_n[best], 4), "splitk_num_splits": best, "heuristic_num_splits": heur,

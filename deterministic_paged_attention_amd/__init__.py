@@ -70,6 +70,7 @@ _sig("bi_kv_write_paged", c_i32, c_vp, c_vp, c_i64, c_vp, c_i64, c_vp, c_i32, c_
 _sig("bi_paged_attention_workspace_size", c_i32, c_vp, c_i32, c_i32, c_i32, ctypes.POINTER(c_sz))
 _sig("bi_paged_attention_item_blocks", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
 _sig("bi_paged_attention_mapping", c_i32, c_vp, c_i32, c_i32, c_i32, P_i32)
+_sig("bi_paged_attention_force_mapping", c_i32, c_i32)
 _ATTN_ARGS = (c_vp, c_vp, c_i64, c_vp, c_vp, c_i32, c_vp, c_i32, c_vp, c_vp, c_i32, c_i32, c_i32)
 _sig("bi_paged_attention", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp, c_vp)
 _sig("bi_paged_attention_split", c_i32, *_ATTN_ARGS, c_vp, c_sz, c_vp)
@@ -345,6 +346,26 @@ def bi_paged_attention_mapping(cfg: AttnConfig, num_seqs: int, num_tokens: int, 
     v = c_i32()
     _check(lib.bi_paged_attention_mapping(cfg.handle, num_seqs, num_tokens, max_seq_len, ctypes.byref(v)))
     return v.value
+
+
+def bi_paged_attention_force_mapping(mapping: int) -> None:
+    """Force the attention work mapping on this thread (0 = chosen per call)."""
+    _check(lib.bi_paged_attention_force_mapping(mapping))
+
+
+class forced_mapping:
+    """Context manager: attention calls inside use the given work mapping."""
+
+    def __init__(self, mapping: int):
+        self.mapping = mapping
+
+    def __enter__(self):
+        bi_paged_attention_force_mapping(self.mapping)
+        return self
+
+    def __exit__(self, *exc):
+        bi_paged_attention_force_mapping(0)
+        return False
 
 
 def bi_splitk_attention_heuristic(cfg: AttnConfig, num_seqs, max_seq_len, num_compute_units, waves_per_cu=8):

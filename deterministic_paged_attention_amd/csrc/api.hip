@@ -26,6 +26,9 @@ struct bi_attn_config {
 namespace {
 
 thread_local std::string g_last_error;
+// Split-phase mapping forced by bi_paged_attention_force_mapping (0: chosen
+// per launch).
+thread_local int32_t g_force_kind = 0;
 
 bi_status fail(bi_status st, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
 bi_status fail(bi_status st, const char* fmt, ...) {
@@ -280,8 +283,12 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
   a.split = cfg->desc.split_size;
   a.window = cfg->desc.window;
   a.ns = (int32_t)((max_seq_len + (int64_t)cfg->desc.split_size - 1) / cfg->desc.split_size);
+  a.force_kind = g_force_kind;
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(BI_ERR_HIP, "no usable device to size the launch");
   const int qb = bi::attn_item_blocks(cfg->desc.head_dim, a);
-  if (qb <= 0) return fail(BI_ERR_HIP, "no usable device to size the launch");
+  if (qb <= 0)
+    return fail(BI_ERR_UNSUPPORTED_CONFIG, "the forced mapping does not exist at head_dim %d", cfg->desc.head_dim);
   *blocks = qb;
   return ok();
 }
@@ -300,9 +307,17 @@ bi_status bi_paged_attention_mapping(const bi_attn_config* cfg, int32_t num_seqs
   a.split = cfg->desc.split_size;
   a.window = cfg->desc.window;
   a.ns = (int32_t)((max_seq_len + (int64_t)cfg->desc.split_size - 1) / cfg->desc.split_size);
+  a.force_kind = g_force_kind;
   int dev = -1;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) return fail(BI_ERR_HIP, "no usable device to size the launch");
-  *mapping = bi::attn_rowgroup_applies(cfg->desc.head_dim, a) ? 1 : 0;
+  *mapping = g_force_kind == 0 && bi::attn_rowgroup_applies(cfg->desc.head_dim, a) ? 1 : 0;
+  return ok();
+}
+
+bi_status bi_paged_attention_force_mapping(int32_t mapping) {
+  if (mapping != 0 && mapping != 1 && mapping != 4 && mapping != 8)
+    return fail(BI_ERR_INVALID_ARG, "mapping must be 0, 1, 4 or 8 (got %d)", mapping);
+  g_force_kind = mapping;
   return ok();
 }
 
@@ -364,7 +379,12 @@ bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split,
   a.ws_acc = (float*)((char*)ws + L.acc_offset);
   a.plan = (int32_t*)((char*)ws + L.plan_offset);
   a.out = (uint16_t*)out;
-  if (fused && out && aligned(out, 8) && bi::attn_rowgroup_applies(cfg->desc.head_dim, a)) {
+  a.rg_static_rounds = 0;
+  a.force_kind = g_force_kind;
+  if ((g_force_kind == 4 || g_force_kind == 8) && cfg->desc.head_dim > 128)
+    return fail(BI_ERR_UNSUPPORTED_CONFIG, "the forced mapping %d does not exist at head_dim %d", g_force_kind,
+                cfg->desc.head_dim);
+  if (g_force_kind == 0 && fused && out && aligned(out, 8) && bi::attn_rowgroup_applies(cfg->desc.head_dim, a)) {
     *fused = true;
     return hip_status(bi::launch_attn_rowgroup(cfg->desc.head_dim, a, stream), "attention row-group launch");
   }

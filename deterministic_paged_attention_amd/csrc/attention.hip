@@ -723,7 +723,11 @@ struct TileCursor {
 };
 
 // This wave's chunks (w, w + 4, ...) of the cursor's tile into ring slot `slot`,
-// through the page resources load_tile would use.
+// through the page resources load_tile would use.  Chunk j of a tile is KiB
+// j % KCH of page j / KCH (K page 0, K page 1, V page 0, V page 1).  The
+// resources are named, not an array: an array indexed by the wave number
+// would leave the scalar registers, and every copy would then be issued
+// through a loop that reads the resource back one lane at a time.
 template <int D>
 __device__ __forceinline__ void shared_issue(const AttnSplitArgs& a, const TileCursor& lc, char* ring, int slot,
                                              int w, int lane) {
@@ -731,7 +735,7 @@ __device__ __forceinline__ void shared_issue(const AttnSplitArgs& a, const TileC
   constexpr int PAGE_BYTES = D * 16 * 2;
   const int64_t head_elems = (int64_t)D * 16;
   const int2 pid = tile_pages(lc.it.pt_row, lc.it.last_entry, lc.t);
-  __amdgpu_buffer_rsrc_t rs[4];  // K page 0, K page 1, V page 0, V page 1
+  __amdgpu_buffer_rsrc_t rk0, rk1, rv0, rv1;
 #pragma unroll
   for (int b = 0; b < 2; ++b) {
     const int entry = 2 * lc.t + b;
@@ -740,15 +744,25 @@ __device__ __forceinline__ void shared_issue(const AttnSplitArgs& a, const TileC
     const bool ok = lc.it.valid && lc.t < lc.it.tile_end && entry * 16 < lc.it.k_len && entry < a.pt_stride &&
                     raw == pgc;
     const int64_t base = ((int64_t)pgc * a.num_kv_heads + lc.it.kvh) * head_elems;
-    rs[b] = page_rsrc(a.k_cache + base, ok ? PAGE_BYTES : 0);
-    rs[2 + b] = page_rsrc(a.v_cache + base, ok ? PAGE_BYTES : 0);
+    const __amdgpu_buffer_rsrc_t kr = page_rsrc(a.k_cache + base, ok ? PAGE_BYTES : 0);
+    const __amdgpu_buffer_rsrc_t vr = page_rsrc(a.v_cache + base, ok ? PAGE_BYTES : 0);
+    if (b == 0) {
+      rk0 = kr;
+      rv0 = vr;
+    } else {
+      rk1 = kr;
+      rv1 = vr;
+    }
   }
 #pragma unroll
   for (int k = 0; k < S::CPW; ++k) {
     const int j = w + kSharedWaves * k;  // chunk of the tile
+    // Page of the chunk: a constant when a page holds a multiple of four
+    // chunks (w < 4 stays inside one page), else chosen by a uniform select.
+    const int page = S::KCH % kSharedWaves == 0 ? (kSharedWaves * k) / S::KCH : j / S::KCH;
+    const __amdgpu_buffer_rsrc_t rs = page == 0 ? rk0 : (page == 1 ? rk1 : (page == 2 ? rv0 : rv1));
     lds_void_t* dst = (lds_void_t*)(ring + slot * S::TILE + j * 1024);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs[j / S::KCH], dst, 16, (j % S::KCH) * 1024 + lane * 16, 0, 0,
-                                             kStreamLoad);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, dst, 16, (j % S::KCH) * 1024 + lane * 16, 0, 0, kStreamLoad);
   }
 }
 
@@ -1422,31 +1436,54 @@ int resident_shared_groups() {
   return cached[dev];
 }
 
+// Split-phase kernels by work mapping (the value is the query-row blocks per
+// item); each gives every row the same bits.
+constexpr int kKindOneBlock = 1;        // attn_split_kernel<D, 1>
+constexpr int kKindWide = kWideBlocks;  // attn_split_kernel<D, 4>
+constexpr int kKindShared = kSharedBlocks;  // attn_split_shared_kernel<D>
+
+// The mapping for a launch: a forced one (diagnostic; 0 when it does not
+// exist at this head size), else shared tiles when the batch is
+// prefill-shaped (on average a full item per sequence) with an item per
+// resident workgroup, wide items when it has four blocks per sequence and an
+// item per resident wave, one-block items otherwise.  Item counts are
+// host-side estimates (every row meeting all ns splits).
 template <int D>
-int item_blocks(const AttnSplitArgs& a) {
+int split_kind(const AttnSplitArgs& a) {
+  if (a.force_kind != 0) {
+    if (a.force_kind == kKindOneBlock) return a.force_kind;
+    if ((a.force_kind == kKindWide || a.force_kind == kKindShared) && D <= 128) return a.force_kind;
+    return 0;
+  }
   if constexpr (D <= 128) {
     const int64_t tq = kRowsPerBlock >> a.log2_group;
-    // shared tiles: on average a full item per sequence and an item per resident workgroup
     const int64_t shared_items = ((int64_t)a.num_tokens + kSharedBlocks * tq - 1) / (kSharedBlocks * tq) *
                                  a.num_kv_heads * a.ns;
     if ((int64_t)a.num_tokens >= kSharedBlocks * tq * (int64_t)a.num_seqs &&
         shared_items >= (int64_t)resident_shared_groups<D>())
-      return kSharedBlocks;
+      return kKindShared;
     const int64_t wide_items = ((int64_t)a.num_tokens + kWideBlocks * tq - 1) / (kWideBlocks * tq) *
                                a.num_kv_heads * a.ns;
     const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
     if ((int64_t)a.num_tokens >= kWideBlocks * tq * (int64_t)a.num_seqs && wide_items >= wide_waves)
-      return kWideBlocks;
+      return kKindWide;
   }
-  return 1;
+  return kKindOneBlock;
+}
+
+template <int D>
+int item_blocks(const AttnSplitArgs& a) {
+  return split_kind<D>(a);
 }
 
 template <int D>
 hipError_t shared_launch(AttnSplitArgs a, hipStream_t stream) {
   a.qblocks = kSharedBlocks;
   a.spread = 0;
-  const int groups = resident_shared_groups<D>();
+  int groups = resident_shared_groups<D>();
   if (groups <= 0) return hipErrorInvalidDevice;
+  // Workgroup g takes items g, g + G, ...: no more workgroups than items.
+  groups = (int)std::min<int64_t>(groups, std::max<int64_t>(1, item_bound(a, kSharedBlocks)));
   if (a.num_seqs > kScanPlanSeqs) {
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
     hipError_t e = hipGetLastError();
@@ -1458,12 +1495,13 @@ hipError_t shared_launch(AttnSplitArgs a, hipStream_t stream) {
 
 template <int D>
 hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
+  const int kind = split_kind<D>(a);
   if constexpr (D <= 128) {
-    const int qb = item_blocks<D>(a);
-    if (qb == kSharedBlocks) return shared_launch<D>(a, stream);
-    if (qb == kWideBlocks) return split_launch_qb<D, kWideBlocks>(a, stream);
+    if (kind == kKindShared) return shared_launch<D>(a, stream);
+    if (kind == kKindWide) return split_launch_qb<D, kWideBlocks>(a, stream);
   }
-  return split_launch_qb<D, 1>(a, stream);
+  if (kind == kKindOneBlock) return split_launch_qb<D, 1>(a, stream);
+  return hipErrorInvalidValue;
 }
 
 template <int D>

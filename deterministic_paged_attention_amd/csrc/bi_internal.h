@@ -40,6 +40,7 @@ struct AttnSplitArgs {
   int32_t spread;            // 1: consecutive items go to different workgroups (set by the launcher)
   uint16_t* out;             // bf16 [T][H_q][D]: written directly by the row-group decode mapping
   int32_t rg_static_rounds;  // row-group mapping: rounds of row groups dealt statically (set by the launcher)
+  int32_t force_kind;        // diagnostic: 0 = choose the split-phase mapping; else 1, 4 or 8 blocks per item
 };
 
 struct AttnMergeArgs {
@@ -64,7 +65,9 @@ hipError_t launch_attn_split(int head_dim, const AttnSplitArgs& a, hipStream_t s
 bool attn_rowgroup_applies(int head_dim, const AttnSplitArgs& a);
 hipError_t launch_attn_rowgroup(int head_dim, const AttnSplitArgs& a, hipStream_t stream);
 // Query-row blocks per work item the split launch would use for these arguments
-// (needs the current device; 0 on failure).
+// (1 one-block items, 4 wide items, 8 shared-tile items; needs the current
+// device; 0 on failure or when a forced mapping does not exist at this head
+// size, where the launch fails too).
 int attn_item_blocks(int head_dim, const AttnSplitArgs& a);
 hipError_t launch_attn_merge(int head_dim, const AttnMergeArgs& a, hipStream_t stream);
 

@@ -210,12 +210,12 @@ bi_status bi_paged_attention_noalloc(const bi_attn_config* cfg,
 /* Work mapping of the split phase (diagnostic).  A work item is one
  * (sequence, group of query-row blocks, KV head, split); *blocks receives the
  * number of 16-column query-row blocks per item the split phase would use for
- * a batch of this shape: 1 for decode-shaped batches, 4 for prefill-shaped ones
- * at head_dim <= 128, so that one loaded K/V tile serves four blocks.  Either
- * mapping performs the same arithmetic for every row (each block runs the same
- * per-tile computation on its own state; tiles outside a row's key range leave
- * it unchanged), so the value affects speed only.  Needs a current device
- * (BI_ERR_HIP without one). */
+ * a batch of this shape: 1 for decode-shaped batches, 4 or 8 for
+ * prefill-shaped ones at head_dim <= 128, so that one loaded K/V tile serves
+ * four or eight blocks.  Every mapping performs the same arithmetic for every
+ * row (each block runs the same per-tile computation on its own state; tiles
+ * outside a row's key range leave it unchanged), so the value affects speed
+ * only.  Needs a current device (BI_ERR_HIP without one). */
 bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                          int32_t max_seq_len, int32_t* blocks);
 
@@ -233,6 +233,19 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
  * Both mappings give every row the same bits.  Needs a current device. */
 bi_status bi_paged_attention_mapping(const bi_attn_config* cfg, int32_t num_seqs, int32_t num_tokens,
                                     int32_t max_seq_len, int32_t* mapping);
+
+/* Force the work mapping of the attention calls made afterwards on the calling
+ * thread (diagnostic; Vosti deep-dive blog, §8.1: work mappings with the same
+ * accumulation order must agree bit for bit, and forcing lets one batch run
+ * through each).  mapping: 0 = chosen per call (the default); otherwise the
+ * split phase takes items of that many query-row blocks: 1 = one-block items,
+ * one wave each; 4 = wide items; 8 = shared-tile items.  While a
+ * mapping is forced, bi_paged_attention and its no-allocation form never take
+ * the row-group mapping, and the split phase of every call (the split-K
+ * comparator's too) uses the forced one; 4 and 8 exist only for head_dim <=
+ * 128 (calls at 256 then fail with BI_ERR_UNSUPPORTED_CONFIG).  No forced
+ * mapping changes any result bit.  BI_ERR_INVALID_ARG for other values. */
+bi_status bi_paged_attention_force_mapping(int32_t mapping);
 
 /* The two phases of bi_paged_attention, separately: the split phase writes the
  * workspace partials described above; the merge phase reads them and writes

@@ -176,6 +176,9 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.bi_paged_attention_mapping(cfg.handle, 0, 16, 64, ctypes.byref(out)) == 1       # no sequences
     assert L.bi_paged_attention_mapping(cfg.handle, 4, 4, 64, None) == 1                    # no result slot
     assert out.value == -1
+    for bad in (-1, 2, 3, 5, 16):
+        assert L.bi_paged_attention_force_mapping(bad) == 1                                  # no such mapping
+    assert L.bi_paged_attention_force_mapping(0) == 0
     assert L.bi_kv_write(cfg.handle, FAKE, 100, FAKE, 1024, FAKE, 3, FAKE, FAKE, 10, None) == 1
     assert L.bi_kv_write(cfg.handle, FAKE, 1024, FAKE, 1024, FAKE, 3, FAKE + 4, FAKE, 10, None) == 1
     assert L.bi_slot_mapping(FAKE, 4, FAKE, FAKE, 2, 3, 32, 10, FAKE, None) == 2      # page size 32

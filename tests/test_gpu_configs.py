@@ -224,6 +224,80 @@ def test_row_group_mapping_lengths_past_max_seq_len():
     assert bool((got[7].float() == 0).all())
 
 
+# ---------------------------------------------------------------- every split-phase mapping on one batch
+
+def _random_batch(Hq, Hk, D, q_lens, k_lens, seed, window=0):
+    """Queries of q_lens[s] tokens at the end of k_lens[s]-token sequences over
+    a randomly permuted page pool (K/V ~ N(0,1)); returns the call arguments
+    and the per-sequence page lists."""
+    cfg = bi.AttnConfig(Hq, Hk, D, split_size=256, window=window)
+    need = [synth.pages_needed(L, 16) for L in k_lens]
+    num_pages = sum(need) + 7
+    perm = synth.permutation(num_pages, seed)
+    pages, cur = [], 0
+    for n in need:
+        pages.append(perm[cur:cur + n])
+        cur += n
+    T = sum(q_lens)
+    k = synth.normal_bf16_device(cfg.k_cache_shape(num_pages), seed + 1)
+    v = synth.normal_bf16_device(cfg.v_cache_shape(num_pages), seed + 2)
+    q = synth.normal_bf16_device((T, Hq, D), seed + 3)
+    pt = page_table_tensor(pages, max(need) + 2, fill=-3).to(DEV)
+    sl = torch.tensor(k_lens, dtype=torch.int32, device=DEV)
+    qsl = torch.tensor(np.concatenate([[0], np.cumsum(q_lens)]), dtype=torch.int32, device=DEV)
+    return cfg, (q, k, v, pt, sl, qsl, max(k_lens)), pages
+
+
+@pytest.mark.parametrize("Hq,Hk,D,B,lo,hi,window", [
+    (32, 8, 128, 1, 8000, 8192, 0),        # the headline layer, one sequence
+    (32, 8, 128, 8, 512, 1500, 0),
+    (8, 4, 256, 4, 15000, 17000, 1024),    # Gemma-shaped local layer at the agentic batch
+    (4, 2, 64, 16, 17, 3000, 0),
+    (16, 1, 64, 3, 50, 1500, 100)])
+def test_small_decode_batches_through_every_split_mapping(Hq, Hk, D, B, lo, hi, window):
+    """Small decode batches forced through one-block, wide and shared-tile
+    items (the last two exist at head_dim <= 128): every row bitwise equal to
+    the launcher's own choice, and every row against the oracle."""
+    k_lens = synth.uniform_ints(B, lo, hi, 3200 + B + D + window)
+    cfg, args, pages = _random_batch(Hq, Hk, D, [1] * B, k_lens, 3210 + B + D, window)
+    auto = bi.bi_paged_attention(cfg, *args)
+    assert bi.bi_paged_attention_mapping(cfg, B, B, max(k_lens)) == 0
+    for kind in ((1, 4, 8) if D <= 128 else (1,)):
+        with bi.forced_mapping(kind):
+            assert first_mismatch(bi.bi_paged_attention(cfg, *args), auto) is None, kind
+    q = args[0]
+    for s in range(B):
+        idx = torch.tensor(pages[s], dtype=torch.long, device=DEV)
+        kk = args[1].index_select(0, idx).cpu().permute(0, 3, 1, 2, 4).reshape(len(pages[s]), 16, Hk, D)
+        vv = args[2].index_select(0, idx).cpu().permute(0, 4, 1, 2, 5, 3).reshape(len(pages[s]), 16, Hk, D)
+        ref_o = oracle.attention_ref(synth.to_f64(q[s:s + 1].cpu()), synth.to_f64(kk), synth.to_f64(vv),
+                                     np.arange(len(pages[s]))[None, :], [k_lens[s]], [0, 1], Hk, 16, window=window)
+        assert float(np.max(np.abs(synth.to_f64(auto[s:s + 1].cpu()) - ref_o))) <= BF16_TOL, s
+
+
+@pytest.mark.parametrize("D,window", [(128, 0), (64, 100), (256, 1024)])
+def test_prefill_batch_through_every_split_mapping(D, window):
+    """A mixed step (prefill chunks of 1..300 tokens and decode tokens) forced
+    through each split-phase mapping: every row bitwise equal (and a forced
+    mapping that does not exist at head_dim 256 is refused)."""
+    Hq, Hk = (32, 8) if D == 128 else ((4, 2) if D == 64 else (8, 4))
+    q_lens = [300, 1, 37, 1, 128, 5]
+    k_lens = [900, 2100, 600, 45, 1400, 5]
+    cfg, args, _ = _random_batch(Hq, Hk, D, q_lens, k_lens, 3300 + D, window)
+    kinds = (1, 4, 8) if D <= 128 else (1,)
+    outs = {}
+    for kind in kinds:
+        with bi.forced_mapping(kind):
+            outs[kind] = bi.bi_paged_attention(cfg, *args)
+    for kind in kinds:
+        assert first_mismatch(outs[kind], outs[1]) is None, kind
+    assert first_mismatch(bi.bi_paged_attention(cfg, *args), outs[1]) is None
+    if D == 256:
+        with bi.forced_mapping(8):
+            with pytest.raises(bi.BiError):
+                bi.bi_paged_attention(cfg, *args)
+
+
 # ---------------------------------------------------------------- prefill mappings against the oracle
 
 @pytest.mark.parametrize("window", [0, 100])
