@@ -108,6 +108,7 @@ _sig("bi_qk_norm_rope_kv_write", c_i32, c_vp, c_vp, c_i64, c_i32, c_vp, c_vp, c_
 _sig("bi_add", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_add_rmsnorm", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_vp, c_f32, c_i64, c_i64, c_vp, c_i64, c_vp)
 _sig("bi_gated_gelu", c_i32, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_vp)
+_sig("bi_gemm_gated_gelu", c_i32, c_vp, c_i64, c_vp, c_i64, c_vp, c_i64, c_i64, c_i64, c_i64, c_vp)
 _sig("bi_status_string", ctypes.c_char_p, c_i32)
 _sig("bi_last_error_message", ctypes.c_char_p)
 _sig("bi_version", c_i32)
@@ -564,6 +565,22 @@ def bi_gated_gelu(x, out=None, stream=None):
         out = torch.empty((R, F), dtype=torch.bfloat16, device=x.device)
     _check(lib.bi_gated_gelu(_ptr(x), x.stride(0) if R > 1 else F2, _ptr(out), out.stride(0) if R > 1 else F, R, F,
                              _stream(stream)))
+    return out
+
+
+def bi_gemm_gated_gelu(a, w_gu, out=None, stream=None):
+    """gated_gelu(a w_gu^T) for a [gate | up] weight of 2F rows, M <= 16 rows of a."""
+    torch = _torch()
+    _need(a, torch.bfloat16, "a")
+    _need(w_gu, torch.bfloat16, "w_gu")
+    M, K = a.shape
+    F = w_gu.shape[0] // 2
+    if out is None:
+        out = torch.empty((M, F), dtype=torch.bfloat16, device=a.device)
+    if a.stride(1) != 1 or w_gu.stride(1) != 1 or out.stride(1) != 1:
+        raise ValueError("a, w_gu and out need contiguous rows")
+    _check(lib.bi_gemm_gated_gelu(_ptr(a), a.stride(0) if M > 1 else K, _ptr(w_gu), w_gu.stride(0), _ptr(out),
+                                  out.stride(0) if M > 1 else F, M, F, K, _stream(stream)))
     return out
 
 

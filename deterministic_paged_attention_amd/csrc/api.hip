@@ -625,6 +625,19 @@ bi_status bi_gemm(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw
                     "gemm launch");
 }
 
+bi_status bi_gemm_gated_gelu(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw, void* out_dev,
+                             int64_t ldo, int64_t M, int64_t ffn, int64_t K, void* stream) {
+  if (M > 16) return fail(BI_ERR_UNSUPPORTED_CONFIG, "bi_gemm_gated_gelu takes at most 16 rows (M=%lld)", (long long)M);
+  if (ffn < 1 || ldo < ffn) return fail(BI_ERR_INVALID_ARG, "ffn >= 1 and ldo >= ffn required");
+  if (bi_status st = check_gemm(a_dev, lda, w_dev, ldw, out_dev, 2 * ffn, BI_BF16, M, 2 * ffn, K)) return st;
+  // The up rows are addressed ffn rows past the gate rows with 32-bit byte offsets.
+  if ((ffn + 16) * ldw * 2 >= (1LL << 32)) return fail(BI_ERR_OUT_OF_RANGE, "ffn * ldw too large");
+  if (M == 0) return ok();
+  return hip_status(bi::launch_gemm_gated_gelu((const uint16_t*)a_dev, lda, (const uint16_t*)w_dev, ldw,
+                                               (uint16_t*)out_dev, ldo, M, ffn, K, (hipStream_t)stream),
+                    "gemm_gated_gelu launch");
+}
+
 bi_status bi_embedding(const void* table_dev, int64_t vocab, int64_t hidden, const int32_t* ids_dev,
                        int32_t num_tokens, void* out_dev, int64_t ld_out, void* stream) {
   if (vocab < 1 || hidden < 8 || hidden % 8 || num_tokens < 0 || ld_out < hidden || ld_out % 8)

@@ -95,6 +95,11 @@ hipError_t launch_add_rmsnorm(const uint16_t* a, int64_t lda, const uint16_t* b,
 
 // out_kind: 0 = bf16, 1 = fp32.  k range [k_begin, k_begin + k_len_per_split) per
 // blockIdx.z when k_splits > 1 (partials to fp32 [k_splits][M][N], ldc = N).
+// out[m, i] = gated_gelu((a w^T)[m, i], (a w^T)[m, F + i]) for a [gate | up]
+// weight w of 2F rows, each product rounded to bf16 first: the bits of
+// launch_gemm (bf16 out) followed by launch_gated_gelu, in one launch; M <= 16.
+hipError_t launch_gemm_gated_gelu(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, uint16_t* out,
+                                  int64_t ldo, int64_t M, int64_t F, int64_t K, hipStream_t stream);
 hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, void* c,
                        int64_t ldc, int out_kind, int64_t M, int64_t N, int64_t K,
                        hipStream_t stream);

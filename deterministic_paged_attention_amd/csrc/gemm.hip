@@ -29,6 +29,7 @@
 // its reduction order follows the number of splits.
 
 #include "bi_internal.h"
+#include "gelu.h"
 
 namespace bi {
 namespace {
@@ -332,17 +333,31 @@ __global__ __launch_bounds__(64 * NW) void gemm_ring_kernel(const uint16_t* a, i
 // as the ring mapping (A operand = 16 rows of w, B operand = the rows of a,
 // k-slots 8*(lane>>4) .. +7 of each 32-wide step, increasing K).  Rows of a
 // past M are not loaded: they only feed output columns that are discarded.
+//
+// GLU: the gated form for a [gate | up] weight (up half from row up_row): a
+// workgroup owns output features n0 .. n0 + 15, streams gate rows n0 .. and up
+// rows up_row + n0 .. (32 LDS rows per stage), runs two MFMA chains over the
+// same rows of a, and writes bf16(gated_gelu(gate, up)) from the bf16-rounded
+// gate and up values — the bits of this GEMM's bf16 output followed by
+// gated_gelu_kernel, in one launch.  Its slices are 256 wide (BK), so that a
+// ring of four 32-row stages fits the 64 KiB of the 16-row form and two
+// workgroups share a compute unit; a copy instruction then carries the half
+// KiB runs of two rows.
 // ---------------------------------------------------------------------------
 constexpr int kSkinnyBK = 512;
 
-template <int STAGES>
+template <int STAGES, bool GLU = false, int BK = kSkinnyBK>
 __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int64_t lda, const uint16_t* w,
                                                           int64_t ldw, void* c, int64_t ldc, int out_kind, int64_t M,
-                                                          int64_t N, int64_t K, int64_t ksplit_len) {
+                                                          int64_t N, int64_t K, int64_t ksplit_len,
+                                                          int64_t up_row = 0) {
 #if defined(__HIP_DEVICE_COMPILE__)
-  constexpr int BK = kSkinnyBK;
+  static_assert(BK == 512 || BK == 256, "a copy instruction moves 1 KiB: one 512-wide row run or two 256-wide");
   constexpr int SPS = BK / 32;                // MFMA K steps per slice
-  constexpr int STAGE = 16 * BK;              // elements per stage: 16 rows x BK
+  constexpr int WR = GLU ? 32 : 16;           // weight rows per stage
+  constexpr int STAGE = WR * BK;              // elements per stage: WR rows x BK
+  constexpr int RPI = 512 / BK;               // rows per copy instruction
+  constexpr int CPR = BK / 8;                 // 16-byte chunks per row of a slice
   __shared__ __attribute__((aligned(1024))) uint16_t lds[STAGES * STAGE];
   if (ksplit_len > 0) {
     const int64_t k0 = (int64_t)blockIdx.y * ksplit_len;
@@ -361,24 +376,34 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
   const uint32_t lds_base = (uint32_t)(uintptr_t)(lds_void*)lds;
 
   if (wave != 0) {
-    // Copy waves: wave 1 rows 0..5, wave 2 rows 6..10, wave 3 rows 11..15.
-    const int rb = wave == 1 ? 0 : (wave == 2 ? 6 : 11);
-    const int cnt = wave == 1 ? 6 : 5;
-    const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w + n0 * ldw, min<int64_t>(16, N - n0), ldw, K);
+    // Copy waves: copy units (one instruction: RPI rows of a slice) [ub, ub +
+    // cnt) of the WR / RPI = 16 per stage, about a third each (0..5, 6..10,
+    // 11..15); LDS rows 16.. are the GLU form's up rows.
+    constexpr int UNITS = WR / RPI;
+    constexpr int MAXC = (UNITS + 2) / 3;
+    const int ub = ((wave - 1) * UNITS + 2) / 3;
+    const int cnt = (wave * UNITS + 2) / 3 - ub;
+    // One resource from weight row n0: the block's rows (GLU: gate rows, then
+    // the up rows up_row further on, the rows between never read); it ends at
+    // the block's last valid element, so rows past N read as zero.
+    const int64_t nvalid = min<int64_t>(16, N - n0);
+    const __amdgpu_buffer_rsrc_t rw = rows_rsrc(w + n0 * ldw, GLU ? up_row + nvalid : nvalid, ldw, K);
     const __amdgpu_buffer_rsrc_t rzero = rows_rsrc(w, 0, ldw, K);
-    uint32_t voff[6];
+    uint32_t voff[MAXC];
 #pragma unroll
-    for (int i = 0; i < 6; ++i) {
-      const int row = rb + i;
-      voff[i] = (uint32_t)(row * ldw * 2 + ((lane ^ (row & 7)) * 16));   // chunk c of row R lands in slot c ^ (R & 7)
+    for (int i = 0; i < MAXC; ++i) {
+      const int row = RPI * (ub + i) + lane / CPR;  // this lane's LDS row
+      const int64_t wrow = (GLU && row >= 16) ? up_row + (row - 16) : row;
+      // chunk c of LDS row R lands in slot c ^ (R & 7)
+      voff[i] = (uint32_t)(wrow * ldw * 2 + (((lane % CPR) ^ (row & 7)) * 16));
     }
     auto issue = [&](int64_t s) {
       const int st = (int)(s % STAGES);
       const bool live = s < nslices;
 #pragma unroll
-      for (int i = 0; i < 6; ++i) {
+      for (int i = 0; i < MAXC; ++i) {
         if (i >= cnt) break;                  // wave-uniform
-        lds_void* dst = (lds_void*)(lds + st * STAGE + (rb + i) * BK);
+        lds_void* dst = (lds_void*)(lds + st * STAGE + RPI * (ub + i) * BK);
         __builtin_amdgcn_raw_ptr_buffer_load_lds(live ? rw : rzero, dst, 16, voff[i] + (uint32_t)(s * BK * 2), 0,
                                                  0, 0);
       }
@@ -386,8 +411,8 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
 #pragma unroll
     for (int p = 0; p < STAGES - 1; ++p) issue(p);
     for (int64_t s = 0; s < nslices; ++s) {
-      if (cnt == 6) wait_vmcnt<6 * (STAGES - 2)>();
-      else wait_vmcnt<5 * (STAGES - 2)>();
+      if (cnt == MAXC) wait_vmcnt<MAXC * (STAGES - 2)>();
+      else wait_vmcnt<(MAXC - 1) * (STAGES - 2)>();
       __builtin_amdgcn_s_barrier();           // slice s is in LDS; slice s-1 is no longer read
       issue(s + STAGES - 1);
     }
@@ -411,6 +436,7 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
                                               ra, aoff + (uint32_t)((s * BK + 32 * ks) * 2), 0, 0));
   };
   f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+  f32x4 acc_up = {0.f, 0.f, 0.f, 0.f};  // GLU: the up rows' chain (LDS rows 16..31)
   auto slice = [&](int64_t s, u32x4 (&cur)[SPS], u32x4 (&nxt)[SPS]) {
     load_a(s + 1, nxt);                      // next slice's rows of a, in flight during this one
     __builtin_amdgcn_s_barrier();            // slice s of w is in LDS
@@ -429,6 +455,16 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
       for (int ks = 0; ks < SPS; ++ks)
         acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[ks]),
                                                       __builtin_bit_cast(bf16x8, cur[ks]), acc, 0, 0, 0);
+      if constexpr (GLU) {
+        const uint32_t su = sw + (uint32_t)((16 + r) * BK * 2);
+#pragma unroll
+        for (int ks = 0; ks < SPS; ++ks) fw[ks] = lds_read16(su + (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16));
+        lds_wait<0>(fw, cur);
+#pragma unroll
+        for (int ks = 0; ks < SPS; ++ks)
+          acc_up = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[ks]),
+                                                           __builtin_bit_cast(bf16x8, cur[ks]), acc_up, 0, 0, 0);
+      }
     } else {
 #pragma unroll
       for (int ks = 0; ks < SPS; ++ks) {    // static register indices; the guard is wave-uniform
@@ -438,6 +474,13 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
           lds_wait<0>(fw, fa);
           acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fw[0]),
                                                         __builtin_bit_cast(bf16x8, fa[0]), acc, 0, 0, 0);
+          if constexpr (GLU) {
+            u32x4 fu[1] = {lds_read16(sw + (uint32_t)((16 + r) * BK * 2) +
+                                      (uint32_t)(((4 * ks + g4) ^ (r & 7)) * 16))};
+            lds_wait<0>(fu, fa);
+            acc_up = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, fu[0]),
+                                                             __builtin_bit_cast(bf16x8, fa[0]), acc_up, 0, 0, 0);
+          }
         }
       }
     }
@@ -453,6 +496,15 @@ __global__ __launch_bounds__(256) void gemm_skinny_kernel(const uint16_t* a, int
   // Lane holds C^T[n0 + 4*g4 + i][r].
   if (!m_ok) return;
   const int64_t nb = n0 + 4 * g4;
+  if constexpr (GLU) {
+    // gate and up rounded to bf16 as this GEMM's bf16 output is, then the
+    // gated GELU of gated_gelu_kernel, one more bf16 rounding.
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const float g = (float)(__bf16)acc[e], u = (float)(__bf16)acc_up[e];
+      acc[e] = gated_gelu_f32(g, u);
+    }
+  }
   if (out_kind == 1) {
     float* cp = reinterpret_cast<float*>(c) + (int64_t)r * ldc + nb;
     if (nb + 4 <= N && ((reinterpret_cast<uintptr_t>(cp) & 15) == 0)) {
@@ -482,7 +534,8 @@ hipError_t skinny_launch(const uint16_t* a, int64_t lda, const uint16_t* w, int6
                          int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream, int64_t ksplit_len,
                          int64_t nsplit) {
   hipLaunchKernelGGL(gemm_skinny_kernel<STAGES>, dim3((unsigned)((N + 15) / 16), (unsigned)nsplit), dim3(256), 0,
-                     stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K, nsplit > 1 ? ksplit_len : (int64_t)0);
+                     stream, a, lda, w, ldw, c, ldc, out_kind, M, N, K, nsplit > 1 ? ksplit_len : (int64_t)0,
+                     (int64_t)0);
   return hipGetLastError();
 }
 
@@ -625,6 +678,19 @@ hipError_t launch_gemm(const uint16_t* a, int64_t lda, const uint16_t* w, int64_
                        int out_kind, int64_t M, int64_t N, int64_t K, hipStream_t stream) {
   if (M == 0 || N == 0) return hipSuccess;
   return launch_gemm_impl(a, lda, w, ldw, c, ldc, out_kind, M, N, K, 0, 1, stream);
+}
+
+// Ring of the gated skinny form: four stages of 32 weight rows x 256 (16 KiB).
+constexpr int kGluStages = 4;
+constexpr int kGluBK = 256;
+
+hipError_t launch_gemm_gated_gelu(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, uint16_t* out,
+                                  int64_t ldo, int64_t M, int64_t F, int64_t K, hipStream_t stream) {
+  if (M == 0 || F == 0) return hipSuccess;
+  if (M > 16) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((gemm_skinny_kernel<kGluStages, true, kGluBK>), dim3((unsigned)((F + 15) / 16), 1u), dim3(256), 0,
+                     stream, a, lda, w, ldw, (void*)out, ldo, 0, M, F, K, (int64_t)0, F);
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_splitk(const uint16_t* a, int64_t lda, const uint16_t* w, int64_t ldw, float* partial,

@@ -10,6 +10,7 @@
 // never on the batch — and every reduction has a tree fixed by the row size.
 
 #include "bi_internal.h"
+#include "gelu.h"
 
 #include <math.h>
 
@@ -174,9 +175,7 @@ __global__ __launch_bounds__(256) void gated_gelu_kernel(const uint16_t* in, int
   const int64_t r = gid / F, i = gid % F;
   const float x = bf16_to_f32(in[r * ld_in + i]);
   const float u = bf16_to_f32(in[r * ld_in + F + i]);
-  const float inner = 0.7978845608028654f * (x + 0.044715f * x * x * x);
-  const float gl = 0.5f * x * (1.0f + tanhf(inner));
-  out[r * ld_out + i] = f32_to_bf16(gl * u);
+  out[r * ld_out + i] = f32_to_bf16(gated_gelu_f32(x, u));
 }
 
 // Greedy sampling: out[row] = the smallest index i with x[row, i] maximal

@@ -22,8 +22,8 @@ from typing import Dict, List, Optional
 import torch
 
 from . import (AttnConfig, alloc_workspace, bi_add, bi_add_rmsnorm, bi_embedding, bi_gated_gelu, bi_gemm,
-               bi_paged_attention, bi_paged_attention_workspace_size, bi_qk_norm_rope_kv_write, bi_rmsnorm,
-               bi_slot_mapping)
+               bi_gemm_gated_gelu, bi_paged_attention, bi_paged_attention_workspace_size, bi_qk_norm_rope_kv_write,
+               bi_rmsnorm, bi_slot_mapping)
 
 
 @dataclasses.dataclass(frozen=True)
@@ -130,8 +130,13 @@ class Decoder:
                                       workspace=ws)
             o = bi_gemm(attn.view(T, Hq * D), W["w_o"])
             h2, xn2 = bi_add_rmsnorm(h, o, W["g_mlp"], s.eps)
-            gu = bi_gemm(xn2, W["w_gu"])
-            act = bi_gated_gelu(gu)
+            if T <= 16 and not cap:
+                # one launch for the gate/up product and the activation (the same bits)
+                gu = None
+                act = bi_gemm_gated_gelu(xn2, W["w_gu"])
+            else:
+                gu = bi_gemm(xn2, W["w_gu"])
+                act = bi_gated_gelu(gu)
             dn = bi_gemm(act, W["w_down"])
             if layer + 1 < nl:
                 h3, xn = bi_add_rmsnorm(h2, dn, self.w["layers"][layer + 1]["g_attn"], s.eps)

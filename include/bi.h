@@ -352,6 +352,17 @@ bi_status bi_add(const void* a_dev, int64_t lda, const void* b_dev, int64_t ldb,
 bi_status bi_gated_gelu(const void* in_dev, int64_t ld_in, void* out_dev, int64_t ld_out, int64_t rows,
                         int64_t ffn, void* stream);
 
+/* bi_gemm (bf16 output) of a [gate | up] weight followed by bi_gated_gelu, in
+ * one launch, for M <= 16 rows of a: out[m, i] = gelu(g) * u with g, u the
+ * bf16 products of row m of a with rows i and ffn + i of w (w bf16 [2 ffn][K],
+ * row stride ldw; out bf16 [M][ffn], row stride ldo >= ffn).  Every output
+ * bit equals that of the two calls (each product runs bi_gemm's own K path
+ * and is rounded to bf16 before the activation).  The shape rules of bi_gemm
+ * apply, and (ffn + 16) * ldw * 2 < 2^32 (BI_ERR_OUT_OF_RANGE otherwise);
+ * BI_ERR_UNSUPPORTED_CONFIG for M > 16. */
+bi_status bi_gemm_gated_gelu(const void* a_dev, int64_t lda, const void* w_dev, int64_t ldw, void* out_dev,
+                             int64_t ldo, int64_t M, int64_t ffn, int64_t K, void* stream);
+
 /* ------------------------------------------------------------------------ */
 /* Host-side plan checks (host arrays; nothing is launched).                 */
 /* ------------------------------------------------------------------------ */

@@ -166,6 +166,10 @@ def test_other_entry_points_reject_bad_arguments():
     assert L.bi_gemm(FAKE, 4096, FAKE, 4096, FAKE, 14336, 7, 4, 14336, 4096, None) == 1   # dtype
     assert L.bi_gemm(FAKE, 100, FAKE, 4096, FAKE, 14336, 0, 4, 14336, 4096, None) == 1    # lda < K
     assert L.bi_gemm(FAKE, 1 << 23, FAKE, 4096, FAKE, 14336, 0, 4, 14336, 4096, None) == 3  # lda too large
+    assert L.bi_gemm_gated_gelu(FAKE, 2560, FAKE, 2560, FAKE, 10240, 17, 10240, 2560, None) == 2   # M > 16
+    assert L.bi_gemm_gated_gelu(FAKE, 2560, FAKE, 2560, FAKE, 100, 4, 10240, 2560, None) == 1      # ldo < ffn
+    assert L.bi_gemm_gated_gelu(FAKE, 2560, FAKE, 2560, FAKE, 10240, 4, 10240, 2550, None) == 1    # K % 32
+    assert L.bi_gemm_gated_gelu(None, 2560, None, 2560, None, 10240, 0, 10240, 2560, None) == 0    # M = 0
     assert L.bi_gemm_splitk(FAKE, 4096, FAKE, 4096, FAKE, 256, 0, 4, 256, 4096, 3, FAKE, 1 << 30, None) == 1
     assert L.bi_gemm_splitk(FAKE, 4096, FAKE, 4096, FAKE, 256, 0, 4, 256, 4096, 4, FAKE, 16, None) == 5
     cfg = bi.AttnConfig(32, 8, 128)

@@ -295,6 +295,36 @@ def test_rmsnorm_ragged_hidden_and_strides():
     assert (out[:, H:].float() == 0).all()
 
 
+@pytest.mark.parametrize("M,F,K", [(1, 10240, 2560), (4, 10240, 2560), (16, 10240, 2560), (7, 4096, 1024),
+                                   (3, 100, 96), (16, 24, 4128)])
+def test_gemm_gated_gelu_is_gemm_then_gated_gelu(M, F, K):
+    """The gated skinny product (gate and up rows of a [gate | up] weight in one
+    workgroup, the activation in its epilogue) against bi_gemm + bi_gated_gelu,
+    bitwise, with wide-ranging inputs (the activation's tanh saturates), ragged
+    F and a K tail; and against the oracle's gated GELU of the GEMM."""
+    g = torch.Generator(device=DEV)
+    g.manual_seed(M * 131 + F + K)
+    a = (torch.randn(M, K, device=DEV, generator=g) * 2.0).to(torch.bfloat16)
+    w = (torch.randn(2 * F, K, device=DEV, generator=g) * 0.05).to(torch.bfloat16)
+    fused = bi.bi_gemm_gated_gelu(a, w)
+    gu = bi.bi_gemm(a, w)
+    ref = bi.bi_gated_gelu(gu)
+    assert first_mismatch(fused, ref) is None
+    # strided rows of a and out
+    a2 = torch.zeros(M, K + 40, dtype=torch.bfloat16, device=DEV)
+    a2[:, :K] = a
+    out2 = torch.full((M, F + 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    bi.bi_gemm_gated_gelu(a2[:, :K], w, out=out2[:, :F])
+    assert first_mismatch(out2[:, :F], ref) is None
+    assert bool((out2[:, F:].float() == 7.0).all())
+    # oracle: gated GELU of the bf16 products (the GEMM's own rounding taken as given)
+    gu64 = synth.to_f64(gu.cpu())
+    want = oracle.gated_gelu_ref(gu64)
+    a_abs = np.abs(want)
+    tol = np.where(a_abs < 8.0, 2e-2, np.ldexp(1.0, np.frexp(a_abs)[1] - 8))   # 2e-2, one bf16 spacing from 8 on
+    assert bool(np.all(np.abs(synth.to_f64(fused.cpu()) - want) <= tol))
+
+
 @pytest.mark.parametrize("M,H", [(1, 2560), (7, 4096), (256, 2560), (3, 8), (5, 8200), (2, 16384)])
 def test_add_rmsnorm_is_add_then_rmsnorm(M, H):
     """The fused residual add + norm equals the two separate launches bit for
