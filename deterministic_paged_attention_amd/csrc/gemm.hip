@@ -651,7 +651,13 @@ hipError_t launch_gemm_impl(const uint16_t* a, int64_t lda, const uint16_t* w, i
       // 256 of them at M = 256 (Gemma-shaped down projection 2560 x 10240:
       // 62 -> 50 us; 2560 x 2048: 18 -> 15 us); with a second round they lose.
       if (ring_fits<32, 80, 2, 128, 4, 2>(M, N)) return L(ring_launch<32, 80, 2, 128, 4, 2>);
-      if (ring_fits<64, 64, 2, 128, 4>(M, N)) return L(ring_launch<64, 64, 2, 128, 4>);
+      // One round of tiles, as few bytes per compute unit as that allows (each
+      // unit pulls (BM + BN) K 2 bytes through LDS at ~50 GB/s): 64 x 64 tiles
+      // with eight waves (4096 x 4096 at M = 256: 29.4 -> 27.4 us; 4096 x 2560
+      // 22.1 -> 20.4 us), else 64 x 96 tiles (6144 wide: 256 of them at
+      // M = 256; 6144 x 4096 38.6 -> 30.4 us, 6144 x 2560 29.9 -> 23.0 us).
+      if (ring_fits<64, 64, 2, 128, 4, 8>(M, N)) return L(ring_launch<64, 64, 2, 128, 4, 8>);
+      if (ring_fits<64, 96, 2, 128, 4>(M, N)) return L(ring_launch<64, 96, 2, 128, 4>);
       return L(ring_launch<64, 64, 2, 128, 2>);
     }
     if (N < 16384) return L(ring_launch<128, 128, 2, 64, 4, 8>);

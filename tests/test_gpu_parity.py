@@ -401,7 +401,7 @@ def test_gemm_ragged_k_tails_and_strides(M, K):
     assert np.all(got[:, N:] == 7.0)
 
 
-@pytest.mark.parametrize("N", [1000, 8192, 20000])
+@pytest.mark.parametrize("N", [1000, 6144, 8192, 20000])
 def test_gemm_tile_configurations_agree_bitwise(N):
     """The tile configuration follows M and N (every M bracket and N bracket is
     visited here); each row of c must equal, bit for bit, that row computed
