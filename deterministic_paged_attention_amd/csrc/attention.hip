@@ -631,9 +631,13 @@ __global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const Attn
   w.stride = gridDim.x * kSplitWaves;
   // Item u of the first round goes to wave u % kSplitWaves of workgroup
   // u / kSplitWaves, or, when there are fewer items than waves (spread), to
-  // wave u / gridDim.x of workgroup u % gridDim.x, so that a small batch's
-  // items run on as many compute units as possible.
-  w.u = a.spread ? wave * (int)gridDim.x + (int)blockIdx.x : (int)blockIdx.x * kSplitWaves + wave;
+  // rank u / gridDim.x of workgroup u % gridDim.x, so that a small batch's
+  // items run on as many compute units as possible.  Ranks take the waves in
+  // order, rotated by two in the upper half of the grid: the two workgroups a
+  // compute unit holds then start their first items on different SIMDs.
+  const int G = (int)gridDim.x;
+  const int rank = (wave + kSplitWaves - ((int)blockIdx.x >= G / 2 ? 2 : 0)) % kSplitWaves;
+  w.u = a.spread ? rank * G + (int)blockIdx.x : (int)blockIdx.x * kSplitWaves + wave;
   w.cur = decode_item(a, w.pv, w.u, w.total);
   if (!w.cur.valid) return;
   w.begin_item();
@@ -1390,7 +1394,8 @@ int resident_split_groups() {
 // keys).
 inline int64_t item_bound(const AttnSplitArgs& a, int qb) {
   const int64_t tq = (int64_t)(kRowsPerBlock >> a.log2_group) * qb;
-  const int64_t blocks = ((int64_t)a.num_tokens + tq - 1) / tq + a.num_seqs;
+  // a block holds at least one token: at most num_tokens blocks (a decode batch: one per sequence)
+  const int64_t blocks = std::min<int64_t>(a.num_tokens, ((int64_t)a.num_tokens + tq - 1) / tq + a.num_seqs);
   int64_t splits = a.ns;
   if (a.window > 0) splits = std::min<int64_t>(splits, (a.window + tq + a.split - 2) / a.split + 1);
   return blocks * a.num_kv_heads * splits;
