@@ -401,7 +401,7 @@ def test_gemm_ragged_k_tails_and_strides(M, K):
     assert np.all(got[:, N:] == 7.0)
 
 
-@pytest.mark.parametrize("N", [1000, 6144, 8192, 20000])
+@pytest.mark.parametrize("N", [1000, 6144, 8192, 12288, 20000])
 def test_gemm_tile_configurations_agree_bitwise(N):
     """The tile configuration follows M and N (every M bracket and N bracket is
     visited here); each row of c must equal, bit for bit, that row computed
@@ -410,7 +410,7 @@ def test_gemm_tile_configurations_agree_bitwise(N):
     a = synth.normal_bf16_device((300, K), 541)
     w = synth.normal_bf16_device((N, K), 542, std=0.02)
     single = {r: bi.bi_gemm(a[r:r + 1], w, out_dtype=torch.float32) for r in (0, 16, 32, 64, 128, 299)}
-    for M in (16, 17, 33, 65, 129, 257, 300):
+    for M in (16, 17, 33, 65, 100, 129, 257, 300):
         c = bi.bi_gemm(a[:M], w, out_dtype=torch.float32)
         for r, ref in single.items():
             if r < M:
