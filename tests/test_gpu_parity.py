@@ -296,7 +296,7 @@ def test_rmsnorm_ragged_hidden_and_strides():
 
 
 @pytest.mark.parametrize("M,F,K", [(1, 10240, 2560), (4, 10240, 2560), (16, 10240, 2560), (7, 4096, 1024),
-                                   (3, 100, 96), (16, 24, 4128)])
+                                   (3, 100, 96), (16, 24, 4128), (4, 6144, 2048), (5, 14336, 4096)])
 def test_gemm_gated_gelu_is_gemm_then_gated_gelu(M, F, K):
     """The gated skinny product (gate and up rows of a [gate | up] weight in one
     workgroup, the activation in its epilogue) against bi_gemm + bi_gated_gelu,
@@ -418,6 +418,34 @@ def test_gemm_tile_configurations_agree_bitwise(N):
     rows = [0, 299]
     ah, wh = synth.to_f64(a[rows].cpu()), synth.to_f64(w[:64].cpu())
     got = torch.cat([single[r][:, :64] for r in rows]).cpu().double().numpy()
+    assert np.all(np.abs(got - oracle.gemm_ref(ah, wh)) <= 1e-3 * oracle.gemm_abs_ref(ah, wh))
+
+
+@pytest.mark.parametrize("N,K", [(100, 96), (1000, 4128), (2560, 2048), (2560, 10240), (4096, 2560),
+                                 (6144, 4096), (8192, 2560)])
+def test_gemm_skinny_rows_agree_with_tiles_bitwise(N, K):
+    """M <= 16 products run the skinny kernel (16-row weight blocks, a's rows
+    loaded by the computing wave), M = 17 output tiles.  Every row of the
+    skinny product must equal, bit for bit, that row of the M = 17 product, in
+    bf16 and fp32, also through row strides and a ragged last slice of K; and
+    agree with the oracle."""
+    a = synth.normal_bf16_device((17, K), 551 + K)
+    w = synth.normal_bf16_device((N, K), 552 + N, std=0.02)
+    for out_dtype in (torch.bfloat16, torch.float32):
+        tiles = bi.bi_gemm(a, w, out_dtype=out_dtype)
+        for M in (1, 3, 4, 16):
+            c = bi.bi_gemm(a[:M], w, out_dtype=out_dtype)
+            assert first_mismatch(c, tiles[:M]) is None, (M, out_dtype)
+    # strided a and c: rows K + 40 apart, columns past N untouched
+    a2 = torch.zeros(4, K + 40, dtype=torch.bfloat16, device=DEV)
+    a2[:, :K] = a[:4]
+    c2 = torch.full((4, N + 24), 7.0, dtype=torch.bfloat16, device=DEV)
+    bi.bi_gemm(a2[:, :K], w, out=c2[:, :N])
+    assert first_mismatch(c2[:, :N], bi.bi_gemm(a[:4], w)) is None
+    assert bool((c2[:, N:].float() == 7.0).all())
+    cols = sorted({0, 1, N // 3, N // 2 + 5, N - 1})
+    ah, wh = synth.to_f64(a[:4].cpu()), synth.to_f64(w[cols].cpu())
+    got = bi.bi_gemm(a[:4], w, out_dtype=torch.float32)[:, cols].cpu().double().numpy()
     assert np.all(np.abs(got - oracle.gemm_ref(ah, wh)) <= 1e-3 * oracle.gemm_abs_ref(ah, wh))
 
 
