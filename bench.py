@@ -45,6 +45,8 @@ METRIC = "batch-invariant paged-attn decode HBM GB/s (% peak) + overhead vs spli
 MAPPING_NAMES = {0: "split + merge", 1: "row-group"}
 PEAK_HBM_GBPS = 8000.0
 HQ, HKV, D, P, S = 32, 8, 128, 16, 256
+DEFAULT_LOCAL_SPLIT = 128  # the decoder shape's windowed-layer split size
+DEFAULT_GLOBAL_SPLIT = 256  # and its global layers'
 HIDDEN = 4096
 QKV_N = (HQ + 2 * HKV) * D
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "attn_decode_b256_traffic.json")
@@ -693,7 +695,7 @@ def bench_gemma(args):
     torch, bi, synth = _torch_env()
     from deterministic_paged_attention_amd.decoder import Decoder, DecoderShape
     from synth.workloads import decoder_weights
-    s = DecoderShape()
+    s = DecoderShape(split_size=args.global_split, split_size_local=args.local_split)
     B = args.batch
     ctx = synth.uniform_ints(B, 512, 4096, args.seed + 70)
     w = decoder_weights(s.layers, s.hidden, s.q_heads, s.kv_heads, s.head_dim, s.ffn, s.vocab, seed=args.seed + 71)
@@ -749,7 +751,7 @@ def bench_gemma(args):
                    "batch": B, "context_lengths": "U{512..4096}", "mean_context": round(sum(ctx) / B, 1),
                    "layers": s.layers, "hidden": s.hidden, "q_heads": s.q_heads, "kv_heads": s.kv_heads,
                    "head_dim": s.head_dim, "ffn": s.ffn, "vocab": s.vocab, "window": s.window,
-                   "global_layers": n_global},
+                   "global_layers": n_global, "split_size": s.split_size, "split_size_local": s.split_size_local},
         "step_ms": {k: round(v, 4) for k, v in t.items()}, "eager_step_ms": round(eager["median"], 4),
         "roofline": {"bound": "hbm", "achieved": round(nbytes / sec / 1e9, 1), "peak": PEAK_HBM_GBPS, "unit": "GB/s",
                      "frac": round(nbytes / sec / 1e9 / PEAK_HBM_GBPS, 4), "traffic": None,
@@ -803,7 +805,7 @@ def bench_agentic(args):
     from deterministic_paged_attention_amd.decoder import Decoder, DecoderShape
     from deterministic_paged_attention_amd.engine import Engine
     from synth.workloads import decoder_weights
-    s = DecoderShape()
+    s = DecoderShape(split_size=args.global_split, split_size_local=args.local_split)
     S, T = args.sessions, args.turns
     shared_len, prompt_len, turn_in, turn_out = args.shared_tokens, args.prompt_tokens, args.turn_input, args.turn_output
     delay = args.user_delay
@@ -874,7 +876,8 @@ def bench_agentic(args):
         "config": {"workload": "agentic sessions on a gemma-3-4b-shaped decoder (random init) through the engine",
                    "sessions": S, "turns": T, "shared_prefix_tokens": shared_len, "first_prompt_tokens": prompt_len,
                    "turn_input_tokens": turn_in, "turn_output_tokens": turn_out, "user_delay_s": delay,
-                   "prefill_budget": args.prefill_budget},
+                   "prefill_budget": args.prefill_budget, "split_size": s.split_size,
+                   "split_size_local": s.split_size_local},
         "session_time_s": round(max(done_at.values()), 3), "engine_time_s": round(engine_time, 3),
         "decode_share_of_engine_time": round(t_decode / engine_time, 4),
         "decode_steps": n_decode_steps, "steps_with_prefill": n_mixed_steps,
@@ -899,6 +902,10 @@ def main():
     ap.add_argument("--user-delay", type=float, default=0.5)
     ap.add_argument("--prefill-budget", type=int, default=2048)
     ap.add_argument("--batch", type=int, default=256)
+    ap.add_argument("--local-split", type=int, default=DEFAULT_LOCAL_SPLIT,
+                    help="gemma and agentic workloads: fixed KV split size of the windowed layers")
+    ap.add_argument("--global-split", type=int, default=DEFAULT_GLOBAL_SPLIT,
+                    help="gemma and agentic workloads: fixed KV split size of the global layers")
     ap.add_argument("--batches", default="1,8,64,256", help="decode-sweep workload: batch sizes to run")
     ap.add_argument("--ms", default="1,7,64,256,1024", help="gemm workload: token counts M to run")
     ap.add_argument("--budgets", default="16,128,512,0",

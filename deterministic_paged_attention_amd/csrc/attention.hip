@@ -209,9 +209,12 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // so m and l come out bit-for-bit the same and acc gains only +-0 terms, which
 // can change nothing but the sign of an exact-zero accumulator; the merge adds
 // such an accumulator into a sum that starts at +0 and stores -0 as +0, so every
-// output bit is the same either way.  (Which form a kernel uses is a matter of
-// its register allocation: without them the one-block decode kernel spills to
-// the accumulator file, with them the shared-tile kernel is slower.)
+// output bit is the same either way.  (Which form a kernel uses is measured:
+// without the selects each PV product accumulates in place, while with them
+// every product goes through a temporary that the next one waits for — a
+// one-block tile at head dim 128 computed alone takes 418 instead of 644 ns,
+// two blocks 673 instead of 1192 ns — but the four-block kernel then spills
+// and the row-group kernel ran no faster.)
 //
 // Two wave-uniform shortcuts leave every value bit-for-bit as computed in
 // full: the key masks are applied only when some row of the wave does not see
@@ -590,7 +593,7 @@ struct SplitWave {
     const int lend = (in_cur || nxt.valid) ? L.tile_end : lt;  // dead load past the last item
     load_tile(a, L.kvh, L.k_len, lt, lend, tile_pages(L.pt_row, L.last_entry, lt), lane, Bl);
     __builtin_amdgcn_sched_barrier(0);
-    compute_tile<D, QB>(st, Bc, curL, ct, g4, a.qk_scale_log2);
+    compute_tile<D, QB, (QB > 1)>(st, Bc, curL, ct, g4, a.qk_scale_log2);
     __builtin_amdgcn_sched_barrier(0);
     if (in_cur) {
       ++ct;

@@ -42,6 +42,7 @@ class DecoderShape:
     eps: float = 1e-6
     page_size: int = 16
     split_size: int = 256
+    split_size_local: int = 128  # windowed layers: their own fixed split size
 
     def is_global(self, layer: int) -> bool:
         return (layer + 1) % self.global_every == 0
@@ -66,7 +67,8 @@ class Decoder:
         self.shape = shape
         self.w = weights
         s = shape
-        self.cfg_local = AttnConfig(s.q_heads, s.kv_heads, s.head_dim, s.page_size, s.split_size, window=s.window)
+        self.cfg_local = AttnConfig(s.q_heads, s.kv_heads, s.head_dim, s.page_size, s.split_size_local,
+                                    window=s.window)
         self.cfg_global = AttnConfig(s.q_heads, s.kv_heads, s.head_dim, s.page_size, s.split_size, window=0)
 
     def cfg(self, layer: int) -> AttnConfig:
@@ -105,7 +107,8 @@ class Decoder:
             capture[name] = t.clone()
 
         slots = bi_slot_mapping(page_table, seq_lens, query_start_loc, T, s.page_size, num_pages)
-        ws = alloc_workspace(bi_paged_attention_workspace_size(self.cfg_local, seq_lens.shape[0], T, max_seq_len))
+        ws = alloc_workspace(max(bi_paged_attention_workspace_size(c, seq_lens.shape[0], T, max_seq_len)
+                                 for c in (self.cfg_local, self.cfg_global)))
         h = bi_embedding(self.w["embed"], ids)
         if capture is not None:
             keep("embed.out", h)
