@@ -214,7 +214,9 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // every product goes through a temporary that the next one waits for — a
 // one-block tile at head dim 128 computed alone takes 418 instead of 644 ns,
 // two blocks 673 instead of 1192 ns — but the four-block kernel then spills
-// and the row-group kernel ran no faster.)
+// and the row-group kernel ran no faster.  The one-block split kernel takes
+// them out and is held to two workgroups per compute unit at head dim <= 128,
+// which it then fits in 256 registers without spilling.)
 //
 // Two wave-uniform shortcuts leave every value bit-for-bit as computed in
 // full: the key masks are applied only when some row of the wave does not see
@@ -612,7 +614,7 @@ struct SplitWave {
 };
 
 template <int D, int QB>
-__global__ __launch_bounds__(64 * kSplitWaves) void attn_split_kernel(const AttnSplitArgs a) {
+__global__ __launch_bounds__(64 * kSplitWaves, (QB == 1 && D <= 128) ? 2 : 1) void attn_split_kernel(const AttnSplitArgs a) {
   const int lane = threadIdx.x & 63;
   // Wave index, made visibly wave-uniform so everything derived from the
   // item index stays in scalar registers (scalar page-table loads).
