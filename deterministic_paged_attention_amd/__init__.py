@@ -325,14 +325,14 @@ def bi_paged_attention_merge(cfg: AttnConfig, seq_lens, query_start_loc, num_tok
 
 
 def workspace_views(cfg: AttnConfig, workspace, num_tokens: int, num_splits: int):
-    """(ml [R, NS, 2] fp32, acc [R, NS, D] fp32) views of a workspace, per the layout in bi.h."""
+    """(ml [R, NS, 2] fp32, acc [R, NS, D] bf16) views of a workspace, per the layout in bi.h."""
     torch = _torch()
     R = num_tokens * cfg.num_q_heads
     ml_bytes = R * num_splits * 8
     acc_off = (ml_bytes + 255) // 256 * 256
     f = workspace.view(torch.uint8)
     ml = f[:ml_bytes].view(torch.float32).view(R, num_splits, 2)
-    acc = f[acc_off: acc_off + R * num_splits * cfg.head_dim * 4].view(torch.float32).view(R, num_splits, cfg.head_dim)
+    acc = f[acc_off: acc_off + R * num_splits * cfg.head_dim * 2].view(torch.bfloat16).view(R, num_splits, cfg.head_dim)
     return ml, acc
 
 

@@ -66,12 +66,12 @@ struct WsLayout {
   size_t ml_bytes = 0, acc_offset = 0, plan_offset = 0, total = 0;
 };
 
-// ml float2 [R][ns] | pad to 256 | acc float [R][ns][D] | pad to 256 | plan int32 [num_seqs + 1]
+// ml float2 [R][ns] | pad to 256 | acc bf16 [R][ns][D] | pad to 256 | plan int32 [num_seqs + 1]
 WsLayout ws_layout(int head_dim, int64_t rows, int64_t ns, int64_t num_seqs) {
   WsLayout w;
   w.ml_bytes = (size_t)rows * (size_t)ns * sizeof(float) * 2;
   w.acc_offset = round_up(w.ml_bytes, kAlign);
-  w.plan_offset = round_up(w.acc_offset + (size_t)rows * (size_t)ns * (size_t)head_dim * sizeof(float), kAlign);
+  w.plan_offset = round_up(w.acc_offset + (size_t)rows * (size_t)ns * (size_t)head_dim * sizeof(uint16_t), kAlign);
   w.total = w.plan_offset + (size_t)(num_seqs + 1) * sizeof(int32_t);
   return w;
 }
@@ -376,7 +376,7 @@ bi_status run_split(const bi_attn_config* cfg, const AttnCall& c, int32_t split,
   a.ns = ns;
   a.qk_scale_log2 = cfg->qk_scale_log2;
   a.ws_ml = (float2*)ws;
-  a.ws_acc = (float*)((char*)ws + L.acc_offset);
+  a.ws_acc = (uint16_t*)((char*)ws + L.acc_offset);
   a.plan = (int32_t*)((char*)ws + L.plan_offset);
   a.out = (uint16_t*)out;
   a.rg_static_rounds = 0;
@@ -411,7 +411,7 @@ bi_status run_merge(const bi_attn_config* cfg, const int32_t* seq_lens, const in
   a.window = cfg->desc.window;
   a.ns = ns;
   a.ws_ml = (const float2*)ws;
-  a.ws_acc = (const float*)((const char*)ws + L.acc_offset);
+  a.ws_acc = (const uint16_t*)((const char*)ws + L.acc_offset);
   a.out = (uint16_t*)out;
   return hip_status(bi::launch_attn_merge(cfg->desc.head_dim, a, stream), "attention merge launch");
 }

@@ -60,23 +60,16 @@ __device__ __forceinline__ float exp2_hw(float x) { return __builtin_amdgcn_exp2
 typedef const __attribute__((address_space(4))) int32_t* const_i32_ptr;
 __device__ __forceinline__ int ldc(const int32_t* p, int64_t i) { return ((const_i32_ptr)p)[i]; }
 
-// Reductions over the four lanes l, l^16, l^32, l^48 that hold one query row,
+// Maximum over the four lanes l, l^16, l^32, l^48 that hold one query row,
 // with the gfx950 lane-swap instructions (VALU only; no LDS traffic and no
 // wait on the memory counters).  Swapping a value with itself and combining
 // the two results gives every lane of a row the same operands in the same
-// order: (r0 op r1) op (r2 op r3), where ri is the value of lane group i.
+// order: max(max(r0, r1), max(r2, r3)), where ri is the value of lane group i.
 __device__ __forceinline__ float row4_max(float v) {
   const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   v = fmaxf(__uint_as_float(a[0]), __uint_as_float(a[1]));
   const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
-}
-
-__device__ __forceinline__ float row4_sum(float v) {
-  const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  v = __uint_as_float(a[0]) + __uint_as_float(a[1]);
-  const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
-  return __uint_as_float(b[0]) + __uint_as_float(b[1]);
 }
 
 // Largest s with qsl[s] <= t.
@@ -97,18 +90,36 @@ __device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, 
 // ---------------------------------------------------------------------------
 
 // Online-softmax state of the query row held by this lane (the four lanes of a
-// row hold identical m and l).
+// row hold identical m and l).  The row sum l is the accumulator of one more
+// PV-shaped product whose A operand is all ones, so all four of its entries
+// hold the same l.
 template <int D>
 struct SplitState {
-  float m, l;
+  float m;
+  f32x4 lacc;
   f32x4 acc[D / 16];
+  __device__ __forceinline__ float l() const { return lacc[0]; }
   __device__ __forceinline__ void init() {
     m = -INFINITY;
-    l = 0.f;
+    lacc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int n = 0; n < D / 16; ++n) acc[n] = f32x4{0.f, 0.f, 0.f, 0.f};
   }
 };
+
+// A split's accumulator goes to the merge (workspace or LDS) as bf16, rounded
+// to nearest even: four consecutive head-dim values per lane, 8 bytes.
+__device__ __forceinline__ u32x2 acc_to_bf16(const f32x4& v) {
+  bf16x4 b;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) b[i] = (__bf16)v[i];
+  return __builtin_bit_cast(u32x2, b);
+}
+
+__device__ __forceinline__ f32x4 bf16_to_acc(const u32x2& w) {
+  return f32x4{__uint_as_float(w.x << 16), __uint_as_float(w.x & 0xffff0000u), __uint_as_float(w.y << 16),
+               __uint_as_float(w.y & 0xffff0000u)};
+}
 
 // Operands of one 32-key tile (two pages of 16 keys) for this lane.
 template <int D>
@@ -204,19 +215,32 @@ __device__ __forceinline__ void load_tile(const AttnSplitArgs& a, int kvh, int k
 // order, it would alone.  A row with no visible key in the tile keeps
 // (m, l, acc) bit-for-bit (select, not update).
 //
+// Per row, with raw scores s_k = q . k_k of the tile's visible keys and
+// c = qk_scale * log2(e):
+//   m_new = max(m, c * max_k s_k)       (= max_k of c * s_k: rounding is monotone)
+//   alpha = 2^(m - m_new)               (0 while the row has seen no key)
+//   P_k   = bf16(2^(fma(s_k, c, -m_new)))
+//   l     = alpha * l + sum_k P_k,   acc = alpha * acc + V^T P
+// where both sums run through the MFMA unit: l is the product of an all-ones
+// A operand with the same P fragment, so it sums exactly the bf16 weights the
+// PV product applies.  A masked score is -inf and gives P = 0; a row whose
+// m_new is still -inf (no key seen yet) subtracts 0 instead, so no lane forms
+// -inf - (-inf).
+//
 // KEEP = false drops the keep-state selects: a row with no visible key in the
 // tile then has m_new == m, alpha == 1 (or 0 on a still-empty row) and P == 0,
-// so m and l come out bit-for-bit the same and acc gains only +-0 terms, which
-// can change nothing but the sign of an exact-zero accumulator; the merge adds
-// such an accumulator into a sum that starts at +0 and stores -0 as +0, so every
-// output bit is the same either way.  (Which form a kernel uses is measured:
-// without the selects each PV product accumulates in place, while with them
-// every product goes through a temporary that the next one waits for — a
-// one-block tile at head dim 128 computed alone takes 418 instead of 644 ns,
-// two blocks 673 instead of 1192 ns — but the four-block kernel then spills
-// and the row-group kernel ran no faster.  The one-block split kernel takes
-// them out and is held to two workgroups per compute unit at head dim <= 128,
-// which it then fits in 256 registers without spilling.)
+// so m comes out bit-for-bit the same and l and acc gain only +-0 terms, which
+// can change nothing but the sign of an exact-zero accumulator (l >= 0 sums
+// +0 products and stays as it was); the merge adds such an accumulator into a
+// sum that starts at +0 and stores -0 as +0, so every output bit is the same
+// either way.  (Which form a kernel uses is measured: without the selects each
+// PV product accumulates in place, while with them every product goes through
+// a temporary that the next one waits for — a one-block tile at head dim 128
+// computed alone takes 418 instead of 644 ns, two blocks 673 instead of 1192
+// ns — but the four-block kernel then spills and the row-group kernel ran no
+// faster.  The one-block split kernel takes them out and is held to two
+// workgroups per compute unit at head dim <= 128, which it then fits in 256
+// registers without spilling.)
 //
 // Two wave-uniform shortcuts leave every value bit-for-bit as computed in
 // full: the key masks are applied only when some row of the wave does not see
@@ -236,7 +260,7 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
 #pragma unroll
   for (int b = 0; b < QB; ++b) inside &= L[b].rm.lo <= kb && kb + 31 <= L[b].rm.hi;
   const bool any_masked = __builtin_amdgcn_ballot_w64(!inside) != 0;
-  // Scores: lane holds keys kb + 16h + 4*g4 + i (i = 0..3) of its row.
+  // Raw scores: lane holds keys kb + 16h + 4*g4 + i (i = 0..3) of its row.
   float x[QB][2][4];
 #pragma unroll
   for (int h = 0; h < 2; ++h) {
@@ -250,7 +274,7 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
 #pragma unroll
     for (int b = 0; b < QB; ++b)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) x[b][h][i] = sc[b][i] * qk_scale_log2;
+      for (int i = 0; i < 4; ++i) x[b][h][i] = sc[b][i];
   }
   if (any_masked) {
 #pragma unroll
@@ -273,10 +297,10 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
       for (int i = 0; i < 4; ++i) tmax[b] = fmaxf(tmax[b], x[b][h][i]);
   }
 #pragma unroll
-  for (int b = 0; b < QB; ++b) tmax[b] = row4_max(tmax[b]);
+  for (int b = 0; b < QB; ++b) tmax[b] = row4_max(tmax[b]) * qk_scale_log2;
 
   bool live[QB];
-  float m_new[QB], alpha[QB], rs[QB];
+  float m_new[QB], alpha[QB];
   bf16x8 pfrag[QB];
   bool rescale = false;
 #pragma unroll
@@ -285,25 +309,21 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
     m_new[b] = fmaxf(st[b].m, tmax[b]);
     alpha[b] = (st[b].m == -INFINITY) ? 0.f : exp2_hw(st[b].m - m_new[b]);
     rescale |= st[b].m != -INFINITY && m_new[b] != st[b].m;
+    const float neg_m = m_new[b] == -INFINITY ? 0.f : -m_new[b];
     __bf16 pb[2][4];
-    rs[b] = 0.f;
 #pragma unroll
     for (int h = 0; h < 2; ++h)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const float e = (x[b][h][i] != -INFINITY) ? exp2_hw(x[b][h][i] - m_new[b]) : 0.f;
-        pb[h][i] = (__bf16)e;
-        rs[b] += (float)pb[h][i];
-      }
+      for (int i = 0; i < 4; ++i) pb[h][i] = (__bf16)exp2_hw(__builtin_fmaf(x[b][h][i], qk_scale_log2, neg_m));
     pfrag[b] = bf16x8{pb[0][0], pb[0][1], pb[0][2], pb[0][3], pb[1][0], pb[1][1], pb[1][2], pb[1][3]};
   }
-#pragma unroll
-  for (int b = 0; b < QB; ++b) rs[b] = row4_sum(rs[b]);
   if (__builtin_amdgcn_ballot_w64(rescale) != 0) {
 #pragma unroll
-    for (int b = 0; b < QB; ++b)
+    for (int b = 0; b < QB; ++b) {
+      st[b].lacc = st[b].lacc * alpha[b];
 #pragma unroll
       for (int n = 0; n < NBLK; ++n) st[b].acc[n] = st[b].acc[n] * alpha[b];
+    }
   }
 
 #pragma unroll
@@ -322,11 +342,12 @@ __device__ __forceinline__ void compute_tile(SplitState<D> (&st)[QB], const Tile
       st[b].acc[n] = (!KEEP || live[b]) ? res : st[b].acc[n];
     }
   }
+  const u32x4 ones = {0x3F803F80u, 0x3F803F80u, 0x3F803F80u, 0x3F803F80u};  // bf16 1.0 x 8
 #pragma unroll
   for (int b = 0; b < QB; ++b) {
-    const float l_new = __builtin_fmaf(alpha[b], st[b].l, rs[b]);
+    const f32x4 res = mfma16x16x32(__builtin_bit_cast(bf16x8, ones), pfrag[b], st[b].lacc);
+    st[b].lacc = (!KEEP || live[b]) ? res : st[b].lacc;
     st[b].m = (!KEEP || live[b]) ? m_new[b] : st[b].m;
-    st[b].l = (!KEEP || live[b]) ? l_new : st[b].l;
   }
 }
 
@@ -545,12 +566,12 @@ __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item
   const __amdgpu_buffer_rsrc_t ar =
       __builtin_amdgcn_make_buffer_rsrc(a.ws_acc + idx0 * D, (short)0, 0x7fffffff, 0x00020000);
   if (g4 == 0)
-    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(st.m), __float_as_uint(st.l)}, mr, (int)(rel * 8u), 0,
+    __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(st.m), __float_as_uint(st.l())}, mr, (int)(rel * 8u), 0,
                                           kPartialStore);
 #pragma unroll
   for (int n = 0; n < D / 16; ++n)
-    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, st.acc[n]), ar,
-                                           (int)((rel * D + 16 * n + 4 * g4) * 4u), 0, kPartialStore);
+    __builtin_amdgcn_raw_buffer_store_b64(acc_to_bf16(st.acc[n]), ar, (int)((rel * D + 16 * n + 4 * g4) * 2u), 0,
+                                          kPartialStore);
 }
 
 // ---------------------------------------------------------------------------
@@ -920,7 +941,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
     return;
   }
   const float2* ml = a.ws_ml + row * a.ns;
-  const float* ap = a.ws_acc + row * a.ns * D + 4 * dq;
+  const uint16_t* ap = a.ws_acc + row * a.ns * D + 4 * dq;
   // The maximum: up to 32 splits' m loaded together per round (max is exact in
   // any order, so the grouping changes no bit).
   constexpr int kMaxGroup = 32, kSumGroup = 16;
@@ -938,17 +959,17 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   f32x4 N = {0.f, 0.f, 0.f, 0.f};
   for (int base = sig_lo; base <= sig_hi; base += kSumGroup) {
     float2 v[kSumGroup];
-    f32x4 av[kSumGroup];
+    u32x2 av[kSumGroup];
 #pragma unroll
     for (int j = 0; j < kSumGroup; ++j) {
       if (base + j <= sig_hi) {
         v[j] = ml[base + j];
-        av[j] = *reinterpret_cast<const f32x4*>(ap + (int64_t)(base + j) * D);
+        av[j] = *reinterpret_cast<const u32x2*>(ap + (int64_t)(base + j) * D);
       }
     }
 #pragma unroll
     for (int j = 0; j < kSumGroup; ++j)
-      if (base + j <= sig_hi) merge_fold(mstar, v[j], av[j], L, N);
+      if (base + j <= sig_hi) merge_fold(mstar, v[j], bf16_to_acc(av[j]), L, N);
   }
   *reinterpret_cast<u32x2*>(op) = merge_finish(N, L);
 }
@@ -1005,8 +1026,9 @@ constexpr int kRgSlots = 256;           // row-group descriptors (a ring)
 // workgroup stops waiting altogether, so a broken count costs at most that once.
 constexpr int kRgSpinLimit = 1 << 14;
 
-// Ring entry of one task: acc float [G][D], then (m, l) float2 [G]; 16-byte multiple.
-__host__ __device__ inline int rg_entry_bytes(int D, int G) { return (G * (4 * D + 8) + 15) & ~15; }
+// Ring entry of one task: acc bf16 [G][D] (rounded as for the workspace), then
+// (m, l) float2 [G]; 16-byte multiple.
+__host__ __device__ inline int rg_entry_bytes(int D, int G) { return (G * (2 * D + 8) + 15) & ~15; }
 __host__ __device__ inline int rg_entries(int D, int G) {
   const int c = kRgRingBytes / rg_entry_bytes(D, G);
   return c < kRgMaxEntries ? c : kRgMaxEntries;
@@ -1193,15 +1215,15 @@ struct RgWave {
       float mstar = -INFINITY;
       for (int i = 0; i < n; ++i) {
         const char* ent = ring + ((f + i) % C) * EB;
-        mstar = fmaxf(mstar, reinterpret_cast<const float2*>(ent + G * D * 4)[r].x);
+        mstar = fmaxf(mstar, reinterpret_cast<const float2*>(ent + G * D * 2)[r].x);
       }
       float L = 0.f;
       f32x4 N = {0.f, 0.f, 0.f, 0.f};
       for (int i = 0; i < n; ++i) {
         const char* ent = ring + ((f + i) % C) * EB;
-        const float2 ml = reinterpret_cast<const float2*>(ent + G * D * 4)[r];
-        const f32x4 acc = *reinterpret_cast<const f32x4*>(ent + (r * D + d0) * 4);
-        merge_fold(mstar, ml, acc, L, N);
+        const float2 ml = reinterpret_cast<const float2*>(ent + G * D * 2)[r];
+        const u32x2 acc = *reinterpret_cast<const u32x2*>(ent + (r * D + d0) * 2);
+        merge_fold(mstar, ml, bf16_to_acc(acc), L, N);
       }
       uint16_t* op = a.out + ((int64_t)q0 * a.num_q_heads + (kvh << a.log2_group) + r) * D + d0;
       *reinterpret_cast<u32x2*>(op) = merge_finish(N, L);
@@ -1228,10 +1250,10 @@ struct RgWave {
     const int r = lane & 15;
     if (r < G) {  // the rows of the block's one token: its G heads
       if (g4 == 0)
-        reinterpret_cast<float2*>(ent + G * D * 4)[r] = make_float2(st[0].m, st[0].l);
+        reinterpret_cast<float2*>(ent + G * D * 2)[r] = make_float2(st[0].m, st[0].l());
 #pragma unroll
       for (int n = 0; n < D / 16; ++n)
-        *reinterpret_cast<f32x4*>(ent + (r * D + 16 * n + 4 * g4) * 4) = st[0].acc[n];
+        *reinterpret_cast<u32x2*>(ent + (r * D + 16 * n + 4 * g4) * 2) = acc_to_bf16(st[0].acc[n]);
     }
     // (the group's size is read before the count: once the count is complete
     // another wave may merge the group and its descriptor slot be reused)

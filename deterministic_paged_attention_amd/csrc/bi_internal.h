@@ -34,7 +34,7 @@ struct AttnSplitArgs {
   int32_t ns;                // splits per row in the workspace
   float qk_scale_log2;       // scale * log2(e)
   float2* ws_ml;             // [R][ns]
-  float* ws_acc;             // [R][ns][D]
+  uint16_t* ws_acc;          // [R][ns][D] bf16
   int32_t* plan;             // [num_seqs + 1]: first work item of each sequence, total last
   int32_t qblocks;           // query-row blocks per work item (set by the launcher)
   int32_t spread;            // 1: consecutive items go to different workgroups (set by the launcher)
@@ -53,7 +53,7 @@ struct AttnMergeArgs {
   int32_t window;
   int32_t ns;
   const float2* ws_ml;
-  const float* ws_acc;
+  const uint16_t* ws_acc;
   uint16_t* out;             // bf16 [T][H_q][D]
 };
 

@@ -162,8 +162,9 @@ bi_status bi_kv_write_paged(const bi_attn_config* cfg, const void* k_new_dev, in
 /*   NS = ceil(max_seq_len / S); R = num_tokens * H_q                        */
 /*   ml  : float2 [R][NS]     (m, l) of each split, m in base-2 units:       */
 /*         m = max_j y_j, l = sum_j 2^(y_j - m), y_j = scale*log2(e)*<q,k_j> */
-/*   acc : float  [R][NS][D]  sum_j 2^(y_j - m) v_j, at the first 256-byte   */
-/*         boundary after ml                                                 */
+/*   acc : bf16   [R][NS][D]  sum_j 2^(y_j - m) v_j rounded to nearest even  */
+/*         (the merge reads each split's accumulator in this precision), at  */
+/*         the first 256-byte boundary after ml                              */
 /*   plan: int32  [num_seqs+1] the launch's own schedule (the split phase:  */
 /*         first work item of each sequence; the row-group mapping: the     */
 /*         sequences by visible keys and a claim counter), at the first     */
@@ -224,8 +225,8 @@ bi_status bi_paged_attention_item_blocks(const bi_attn_config* cfg, int32_t num_
  * num_seqs, so every q_len is 1) of at most 2048 sequences with at least two
  * (sequence, KV head) row groups per compute unit, where a row meets few
  * enough splits (all ceil(max_seq_len / S), or with a window those of w keys)
- * that a row group's partials fit the kernel's LDS ring (up to 59 splits for
- * head_dim 128 with 4 query heads per KV head, or head_dim 256 with 2).
+ * that a row group's partials fit the kernel's LDS ring (up to 116 splits for
+ * head_dim 128 with 4 query heads per KV head, 118 for head_dim 256 with 2).
  * There each workgroup computes the splits of whole row groups, keeps their
  * partials in LDS and merges them itself (Vosti deep-dive blog, §8.1: two
  * work mappings with the same accumulation order), writing no partials to the

@@ -52,7 +52,7 @@ def test_workspace_size_matches_documented_layout():
     ns = -(-L // 256)
     R = T * 32
     ml = R * ns * 8
-    acc_end = (ml + 255) // 256 * 256 + R * ns * 128 * 4
+    acc_end = (ml + 255) // 256 * 256 + R * ns * 128 * 2  # acc is bf16
     expect = (acc_end + 255) // 256 * 256 + (B + 1) * 4
     assert bi.bi_paged_attention_workspace_size(cfg, B, T, L) == expect
     assert bi.bi_kv_cache_bytes(cfg, 10) == 10 * 8 * 128 * 16 * 2
@@ -136,7 +136,7 @@ def test_attention_rejects_bad_arguments(kw, status):
 def test_noalloc_attention_rejects_before_any_launch():
     """The allocation-free entry point refuses a call whose partials exceed its
     64 MiB device array (the 8B decode at 256 sequences of up to 8192 keys needs
-    about 136 MB) and bad arguments, before touching the device."""
+    about 69 MB) and bad arguments, before touching the device."""
     cfg = bi.AttnConfig(32, 8, 128)
     L = bi.lib
     args = (cfg.handle, FAKE, 32 * 128, FAKE, FAKE, 10, FAKE, 512, FAKE, FAKE)
