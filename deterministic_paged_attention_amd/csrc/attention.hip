@@ -72,19 +72,6 @@ __device__ __forceinline__ float row4_max(float v) {
   return fmaxf(__uint_as_float(b[0]), __uint_as_float(b[1]));
 }
 
-// Largest s with qsl[s] <= t.
-// (Every sequence has at least one query row, so when there are as many
-// tokens as sequences token t is sequence t's only row: no search.)
-__device__ __forceinline__ int find_token_seq(const int32_t* qsl, int num_seqs, int num_tokens, int t) {
-  if (num_tokens == num_seqs) return t;
-  int lo = 0, hi = num_seqs - 1;
-  while (lo < hi) {
-    const int mid = (lo + hi + 1) >> 1;
-    if (qsl[mid] <= t) lo = mid; else hi = mid - 1;
-  }
-  return lo;
-}
-
 // ---------------------------------------------------------------------------
 // Building blocks of the split phase.
 // ---------------------------------------------------------------------------
@@ -918,23 +905,42 @@ __device__ __forceinline__ u32x2 merge_finish(const f32x4& N, float L) {
 // in increasing order: m* = max m_s, w_s = 2^(m_s - m*), L = sum w_s l_s,
 // N = sum w_s acc_s, o = N / L.  With a single split w = 1 exactly and the
 // result is acc / l.
+//
+// Each wave serves one query token (all its rows share the split range), so
+// the sequence lookup and the split bounds are wave-uniform and go through
+// the scalar unit; a token's H_q rows take ceil(H_q * D / 256) waves.  Up to
+// kOnePass splits every load of a row is issued before any is used (one
+// round trip); beyond that the maxima come first, then the sums in groups.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) {
   constexpr int TPR = D / 4;
-  const int64_t gid = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  const int64_t row = gid / TPR;
-  const int dq = (int)(gid % TPR);
-  if (row >= (int64_t)a.num_tokens * a.num_q_heads) return;
-  const int tok = (int)(row / a.num_q_heads);
-  const int s = find_token_seq(a.qsl, a.num_seqs, a.num_tokens, tok);
-  const int q0 = a.qsl[s];
-  const int q_len = a.qsl[s + 1] - q0;
-  const int k_len = a.seq_lens[s];
+  const int wpt = (a.num_q_heads * TPR + 63) / 64;  // waves per token
+  const int gw = (int)blockIdx.x * 4 + (int)(threadIdx.x >> 6);
+  const int tok = __builtin_amdgcn_readfirstlane(gw / wpt);
+  if (tok >= a.num_tokens) return;
+  const int idx = (gw - tok * wpt) * 64 + (int)(threadIdx.x & 63);
+  const int h = idx / TPR, dq = idx % TPR;
+  if (h >= a.num_q_heads) return;
+  // Largest s with qsl[s] <= tok (every sequence has a query row).
+  int s = 0;
+  if (a.num_tokens == a.num_seqs) {
+    s = tok;
+  } else {
+    int hi = a.num_seqs - 1;
+    while (s < hi) {
+      const int mid = (s + hi + 1) >> 1;
+      if (ldc(a.qsl, mid) <= tok) s = mid; else hi = mid - 1;
+    }
+  }
+  const int q0 = ldc(a.qsl, s);
+  const int q_len = ldc(a.qsl, s + 1) - q0;
+  const int k_len = ldc(a.seq_lens, s);
   const int p = k_len - q_len + (tok - q0);
   const int lo = a.window > 0 ? max(0, p - a.window + 1) : 0;
   const int sig_lo = lo / a.split;
   const int sig_hi = min(p / a.split, a.ns - 1);
+  const int64_t row = (int64_t)tok * a.num_q_heads + h;
   uint16_t* op = a.out + row * D + 4 * dq;
   if (p < 0 || sig_lo > sig_hi) {
     *reinterpret_cast<u32x2*>(op) = u32x2{0u, 0u};
@@ -942,9 +948,32 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   }
   const float2* ml = a.ws_ml + row * a.ns;
   const uint16_t* ap = a.ws_acc + row * a.ns * D + 4 * dq;
+  const int nsp = sig_hi - sig_lo + 1;
+  constexpr int kOnePass = 16, kMaxGroup = 32, kSumGroup = 16;
+  float L = 0.f;
+  f32x4 N = {0.f, 0.f, 0.f, 0.f};
+  if (nsp <= kOnePass) {
+    float2 v[kOnePass];
+    u32x2 av[kOnePass];
+#pragma unroll
+    for (int j = 0; j < kOnePass; ++j) {
+      if (j < nsp) {
+        v[j] = ml[sig_lo + j];
+        av[j] = *reinterpret_cast<const u32x2*>(ap + (int64_t)(sig_lo + j) * D);
+      }
+    }
+    float mstar = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kOnePass; ++j)
+      if (j < nsp) mstar = fmaxf(mstar, v[j].x);
+#pragma unroll
+    for (int j = 0; j < kOnePass; ++j)
+      if (j < nsp) merge_fold(mstar, v[j], bf16_to_acc(av[j]), L, N);
+    *reinterpret_cast<u32x2*>(op) = merge_finish(N, L);
+    return;
+  }
   // The maximum: up to 32 splits' m loaded together per round (max is exact in
   // any order, so the grouping changes no bit).
-  constexpr int kMaxGroup = 32, kSumGroup = 16;
   float mstar = -INFINITY;
   for (int base = sig_lo; base <= sig_hi; base += kMaxGroup) {
     float mv[kMaxGroup];
@@ -955,8 +984,6 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(const AttnMergeArgs a) 
   }
   // The sums, in increasing split order; the loads of up to 16 splits are
   // issued before any of them is accumulated.
-  float L = 0.f;
-  f32x4 N = {0.f, 0.f, 0.f, 0.f};
   for (int base = sig_lo; base <= sig_hi; base += kSumGroup) {
     float2 v[kSumGroup];
     u32x2 av[kSumGroup];
@@ -1538,8 +1565,9 @@ hipError_t split_launch(const AttnSplitArgs& a, hipStream_t stream) {
 
 template <int D>
 hipError_t merge_launch(const AttnMergeArgs& a, hipStream_t stream) {
-  const int64_t threads = (int64_t)a.num_tokens * a.num_q_heads * (D / 4);
-  dim3 grid((unsigned)((threads + 255) / 256));
+  // one wave per (token, 64 threads of its rows), four waves a workgroup
+  const int64_t waves = (int64_t)a.num_tokens * ((a.num_q_heads * (D / 4) + 63) / 64);
+  dim3 grid((unsigned)((waves + 3) / 4));
   hipLaunchKernelGGL(attn_merge_kernel<D>, grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
