@@ -1503,10 +1503,12 @@ constexpr int kKindShared = kSharedBlocks;  // attn_split_shared_kernel<D>
 
 // The mapping for a launch: a forced one (diagnostic; 0 when it does not
 // exist at this head size), else shared tiles when the batch is
-// prefill-shaped (on average a full item per sequence) with an item per two
-// resident workgroups, wide items when it has four blocks per sequence and an
-// item per resident wave, one-block items otherwise.  Item counts are
-// host-side estimates (every row meeting all ns splits).
+// prefill-shaped (on average three quarters of an item per sequence) with an
+// item per two resident workgroups and, where wide items also qualify, at
+// most a fifth more padded blocks than they; wide items when it has four
+// blocks per sequence and an item per resident wave; one-block items
+// otherwise.  Item counts are host-side estimates (every row meeting all ns
+// splits).
 template <int D>
 int split_kind(const AttnSplitArgs& a) {
   if (a.force_kind != 0) {
@@ -1515,19 +1517,27 @@ int split_kind(const AttnSplitArgs& a) {
     return 0;
   }
   if constexpr (D <= 128) {
-    const int64_t tq = kRowsPerBlock >> a.log2_group;
-    const int64_t shared_items = ((int64_t)a.num_tokens + kSharedBlocks * tq - 1) / (kSharedBlocks * tq) *
-                                 a.num_kv_heads * a.ns;
-    // Shared tiles from half a round of resident workgroups on (measured: with 256 items of
-    // 8 blocks they beat one-block items by 7-18%, with 160 or fewer they lose by 8-20%).
-    if ((int64_t)a.num_tokens >= kSharedBlocks * tq * (int64_t)a.num_seqs &&
-        2 * shared_items >= (int64_t)resident_shared_groups<D>())
-      return kKindShared;
-    const int64_t wide_items = ((int64_t)a.num_tokens + kWideBlocks * tq - 1) / (kWideBlocks * tq) *
-                               a.num_kv_heads * a.ns;
+    const int64_t tq = kRowsPerBlock >> a.log2_group;  // query tokens per block
+    const int64_t T = a.num_tokens, B = a.num_seqs;
+    const int64_t shared_items = (T + kSharedBlocks * tq - 1) / (kSharedBlocks * tq) * a.num_kv_heads * a.ns;
+    const int64_t wide_items = (T + kWideBlocks * tq - 1) / (kWideBlocks * tq) * a.num_kv_heads * a.ns;
     const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
-    if ((int64_t)a.num_tokens >= kWideBlocks * tq * (int64_t)a.num_seqs && wide_items >= wide_waves)
-      return kKindWide;
+    // Blocks a sequence of the average query length takes in each form,
+    // padding included: shared tiles are kept while they pad at most a fifth
+    // more than wide items (a shared block costs less than a wide one).
+    const int64_t n = (T + B - 1) / B;
+    const int64_t sb = kSharedBlocks * ((n + kSharedBlocks * tq - 1) / (kSharedBlocks * tq));
+    const int64_t wb = kWideBlocks * ((n + kWideBlocks * tq - 1) / (kWideBlocks * tq));
+    // Shared tiles when sequences bring three quarters of an item on average
+    // and the items fill half a round of resident workgroups (measured: from
+    // 256 items of 8 blocks they beat one-block items by 7-18%, at 160 and
+    // below they lose by 8-20%; at 24 rows per sequence they beat wide items
+    // by 8-30%).
+    const bool shared_ok =
+        4 * T >= 3 * kSharedBlocks * tq * B && 2 * shared_items >= (int64_t)resident_shared_groups<D>();
+    const bool wide_ok = T >= kWideBlocks * tq * B && wide_items >= wide_waves;
+    if (shared_ok && (!wide_ok || 5 * sb <= 6 * wb)) return kKindShared;
+    if (wide_ok) return kKindWide;
   }
   return kKindOneBlock;
 }
