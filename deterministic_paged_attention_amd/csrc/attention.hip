@@ -1503,11 +1503,11 @@ constexpr int kKindShared = kSharedBlocks;  // attn_split_shared_kernel<D>
 
 // The mapping for a launch: a forced one (diagnostic; 0 when it does not
 // exist at this head size), else shared tiles when the batch is
-// prefill-shaped (on average three quarters of an item per sequence) with an
-// item per two resident workgroups and, where wide items also qualify, at
-// most a fifth more padded blocks than they; wide items when it has four
-// blocks per sequence and an item per resident wave; one-block items
-// otherwise.  Item counts are host-side estimates (every row meeting all ns
+// prefill-shaped (on average half an item per sequence) with an item per two
+// resident workgroups and, where wide items also qualify and sequences span
+// more than one item, at most a fifth more padded blocks than they; wide
+// items when it has four blocks per sequence and an item per resident wave;
+// one-block items otherwise.  Item counts are host-side estimates (every row meeting all ns
 // splits).
 template <int D>
 int split_kind(const AttnSplitArgs& a) {
@@ -1523,20 +1523,21 @@ int split_kind(const AttnSplitArgs& a) {
     const int64_t wide_items = (T + kWideBlocks * tq - 1) / (kWideBlocks * tq) * a.num_kv_heads * a.ns;
     const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
     // Blocks a sequence of the average query length takes in each form,
-    // padding included: shared tiles are kept while they pad at most a fifth
-    // more than wide items (a shared block costs less than a wide one).
+    // padding included: past one item a sequence, shared tiles are kept while
+    // they pad at most a fifth more than wide items (a shared block costs less
+    // than a wide one; up to one item they are faster whatever the padding).
     const int64_t n = (T + B - 1) / B;
     const int64_t sb = kSharedBlocks * ((n + kSharedBlocks * tq - 1) / (kSharedBlocks * tq));
     const int64_t wb = kWideBlocks * ((n + kWideBlocks * tq - 1) / (kWideBlocks * tq));
-    // Shared tiles when sequences bring three quarters of an item on average
-    // and the items fill half a round of resident workgroups (measured: from
-    // 256 items of 8 blocks they beat one-block items by 7-18%, at 160 and
-    // below they lose by 8-20%; at 24 rows per sequence they beat wide items
-    // by 8-30%).
+    // Shared tiles when sequences bring half an item on average and the items
+    // fill half a round of resident workgroups (measured: from 256 items of 8
+    // blocks they beat one-block items by 7-18%, at 160 and below they lose by
+    // 8-20%; at 16-24 rows per sequence they beat wide items by 2-30%, at 48
+    // wide items win by 15%).
     const bool shared_ok =
-        4 * T >= 3 * kSharedBlocks * tq * B && 2 * shared_items >= (int64_t)resident_shared_groups<D>();
+        2 * T >= kSharedBlocks * tq * B && 2 * shared_items >= (int64_t)resident_shared_groups<D>();
     const bool wide_ok = T >= kWideBlocks * tq * B && wide_items >= wide_waves;
-    if (shared_ok && (!wide_ok || 5 * sb <= 6 * wb)) return kKindShared;
+    if (shared_ok && (!wide_ok || n <= kSharedBlocks * tq || 5 * sb <= 6 * wb)) return kKindShared;
     if (wide_ok) return kKindWide;
   }
   return kKindOneBlock;
