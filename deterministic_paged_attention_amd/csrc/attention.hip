@@ -555,10 +555,22 @@ __device__ __forceinline__ void write_partial(const AttnSplitArgs& a, const Item
   if (g4 == 0)
     __builtin_amdgcn_raw_buffer_store_b64(u32x2{__float_as_uint(st.m), __float_as_uint(st.l())}, mr, (int)(rel * 8u), 0,
                                           kPartialStore);
+  // Column blocks n and n + 1 in one 16-byte store per lane: lane rows g4 and
+  // g4 ^ 1 (lanes 16 apart) trade halves, so that an even row holds head dims
+  // 16n + 4g4 .. + 7 of block n (its own four, then its partner's) and an odd
+  // row 16(n+1) + 4(g4-1) .. + 7 of block n + 1 (its partner's four, then its
+  // own).  The swap moves odd rows of its first operand and even rows of its
+  // second; either way a lane's words come out as (first, second).
+  const bool odd = (g4 & 1) != 0;
 #pragma unroll
-  for (int n = 0; n < D / 16; ++n)
-    __builtin_amdgcn_raw_buffer_store_b64(acc_to_bf16(st.acc[n]), ar, (int)((rel * D + 16 * n + 4 * g4) * 2u), 0,
-                                          kPartialStore);
+  for (int n = 0; n < D / 16; n += 2) {
+    const u32x2 x = acc_to_bf16(st.acc[n]), y = acc_to_bf16(st.acc[n + 1]);
+    const auto w0 = __builtin_amdgcn_permlane16_swap(x.x, y.x, false, false);
+    const auto w1 = __builtin_amdgcn_permlane16_swap(x.y, y.y, false, false);
+    const u32x4 v = {w0[0], w1[0], w0[1], w1[1]};
+    const uint32_t d0 = odd ? 16 * (n + 1) + 4 * (g4 - 1) : 16 * n + 4 * g4;
+    __builtin_amdgcn_raw_buffer_store_b128(v, ar, (int)((rel * D + d0) * 2u), 0, kPartialStore);
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -1504,10 +1516,9 @@ constexpr int kKindShared = kSharedBlocks;  // attn_split_shared_kernel<D>
 // The mapping for a launch: a forced one (diagnostic; 0 when it does not
 // exist at this head size), else shared tiles when the batch is
 // prefill-shaped (on average half an item per sequence) with an item per two
-// resident workgroups and, where wide items also qualify and sequences span
-// more than one item, at most a fifth more padded blocks than they; wide
-// items when it has four blocks per sequence and an item per resident wave;
-// one-block items otherwise.  Item counts are host-side estimates (every row meeting all ns
+// resident workgroups; wide items when it has four blocks per sequence and an
+// item per resident wave (which, given the first rule, leaves them to forced
+// use); one-block items otherwise.  Item counts are host-side estimates (every row meeting all ns
 // splits).
 template <int D>
 int split_kind(const AttnSplitArgs& a) {
@@ -1522,23 +1533,15 @@ int split_kind(const AttnSplitArgs& a) {
     const int64_t shared_items = (T + kSharedBlocks * tq - 1) / (kSharedBlocks * tq) * a.num_kv_heads * a.ns;
     const int64_t wide_items = (T + kWideBlocks * tq - 1) / (kWideBlocks * tq) * a.num_kv_heads * a.ns;
     const int64_t wide_waves = (int64_t)resident_split_groups<D, kWideBlocks>() * kSplitWaves;
-    // Blocks a sequence of the average query length takes in each form,
-    // padding included: past one item a sequence, shared tiles are kept while
-    // they pad at most a fifth more than wide items (a shared block costs less
-    // than a wide one; up to one item they are faster whatever the padding).
-    const int64_t n = (T + B - 1) / B;
-    const int64_t sb = kSharedBlocks * ((n + kSharedBlocks * tq - 1) / (kSharedBlocks * tq));
-    const int64_t wb = kWideBlocks * ((n + kWideBlocks * tq - 1) / (kWideBlocks * tq));
-    // Shared tiles when sequences bring half an item on average and the items
-    // fill half a round of resident workgroups (measured: from 256 items of 8
-    // blocks they beat one-block items by 7-18%, at 160 and below they lose by
-    // 8-20%; at 16-24 rows per sequence they beat wide items by 2-30%, at 48
-    // wide items win by 15%).
-    const bool shared_ok =
-        2 * T >= kSharedBlocks * tq * B && 2 * shared_items >= (int64_t)resident_shared_groups<D>();
-    const bool wide_ok = T >= kWideBlocks * tq * B && wide_items >= wide_waves;
-    if (shared_ok && (!wide_ok || n <= kSharedBlocks * tq || 5 * sb <= 6 * wb)) return kKindShared;
-    if (wide_ok) return kKindWide;
+    // Shared tiles when sequences bring half an item of rows on average and
+    // the items fill half a round of resident workgroups (measured: from 256
+    // items of 8 blocks they beat one-block items by 7-18%, at 160 and below
+    // they lose by 8-20%; at 16-24 rows per sequence they beat wide items by
+    // 2-30%, and on a batch mixing decode rows with chunks by 30%, though
+    // uniform 48-row chunks ran 15% faster as wide items).
+    if (2 * T >= kSharedBlocks * tq * B && 2 * shared_items >= (int64_t)resident_shared_groups<D>())
+      return kKindShared;
+    if (T >= kWideBlocks * tq * B && wide_items >= wide_waves) return kKindWide;
   }
   return kKindOneBlock;
 }

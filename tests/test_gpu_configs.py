@@ -331,16 +331,21 @@ def test_shared_tile_items_head_dim_64_against_the_oracle():
 
 
 def test_wide_items_against_the_oracle():
-    """A step the launcher maps to four-block items: 40-token chunks at the end
-    of 48 requests of 520..700 tokens."""
+    """Four-block items (a mapping the launcher leaves to forced use: shared-tile
+    items win wherever both apply) against the oracle: 40-token chunks at the
+    end of 48 requests of 520..700 tokens."""
     cfg = bi.AttnConfig(32, 8, 128, split_size=256)
     lengths = synth.uniform_ints(48, 520, 700, 1401)
     reqs = {i: Request(1400 + i, L, LLAMA) for i, L in enumerate(lengths)}
     kv = PagedKV(cfg, sum(synth.pages_needed(L, 16) for L in lengths) + 9, seed=23)
     run_step(kv, reqs, [(i, L - 40) for i, L in enumerate(lengths)], attention=False)
-    assert bi.bi_paged_attention_item_blocks(cfg, 48, 40 * 48, max(lengths)) == 4
-    assert bi.bi_paged_attention_item_blocks(cfg, 48, 24 * 48, max(lengths)) == 8   # 24 rows: shared tiles
-    out = run_step(kv, reqs, [(i, 40) for i in range(48)])
+    assert bi.bi_paged_attention_item_blocks(cfg, 48, 40 * 48, max(lengths)) == 8
+    bi.bi_paged_attention_force_mapping(4)
+    try:
+        assert bi.bi_paged_attention_item_blocks(cfg, 48, 40 * 48, max(lengths)) == 4
+        out = run_step(kv, reqs, [(i, 40) for i in range(48)])
+    finally:
+        bi.bi_paged_attention_force_mapping(0)
     ref = oracle_rows(reqs, list(out.keys()), LLAMA, 0)
     assert _max_err(out, ref) <= BF16_TOL
 

@@ -152,19 +152,24 @@ def test_prefill_chunks_and_token_by_token_agree(geom, window):
 
 
 def test_wide_and_shared_items_agree_with_one_block_items():
-    """48 requests prefilled in 40-token chunks (ten query blocks per sequence:
-    four-block wide items) and in 24-token chunks (six query blocks, padded into
-    eight-block shared-tile items), in one shot (shared-tile items) and token by
-    token (one-block items): every row bitwise equal."""
+    """48 requests prefilled in 40-token chunks through four-block wide items
+    (forced: the launcher takes shared tiles wherever both apply), in 24-token
+    chunks (six query blocks, padded into eight-block shared-tile items), in one
+    shot (shared-tile items) and token by token (one-block items): every row
+    bitwise equal."""
     cfg = bi.AttnConfig(32, 8, 128, split_size=256)
     reqs = _pool(LLAMA, 48, seed=61, lo=520, hi=700)
-    assert bi.bi_paged_attention_item_blocks(cfg, 48, 40 * 48, 700) == 4
     assert bi.bi_paged_attention_item_blocks(cfg, 48, 24 * 48, 700) == 8
     T = sum(r.length for r in reqs.values())
     assert bi.bi_paged_attention_item_blocks(cfg, 48, T, 700) == 8
     one_shot = _run_schedule(cfg, reqs, [[(i, r.length) for i, r in reqs.items()]], page_seed=8)
-    chunked = _run_schedule(cfg, reqs, _chunked(reqs, 40), page_seed=9)
-    assert _assert_same(one_shot, chunked, "40-token chunks vs one shot") == T
+    bi.bi_paged_attention_force_mapping(4)
+    try:
+        assert bi.bi_paged_attention_item_blocks(cfg, 48, 40 * 48, 700) == 4
+        chunked = _run_schedule(cfg, reqs, _chunked(reqs, 40), page_seed=9)
+    finally:
+        bi.bi_paged_attention_force_mapping(0)
+    assert _assert_same(one_shot, chunked, "40-token chunks (wide items) vs one shot") == T
     chunked = _run_schedule(cfg, reqs, _chunked(reqs, 24), page_seed=13)
     assert _assert_same(one_shot, chunked, "24-token chunks vs one shot") == T
     sample = {i: reqs[i] for i in (0, 17, 47)}
