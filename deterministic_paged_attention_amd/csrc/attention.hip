@@ -409,38 +409,31 @@ __global__ __launch_bounds__(1024) void attn_plan_kernel(const AttnSplitArgs a) 
   plan_scan<1024>(a, wave_tot, &carry_sh, [&](int i, int v) { a.plan[i] = v; });
 }
 
-// Up to this many sequences, every workgroup of the split kernel computes the
+// Up to this many sequences, every workgroup of the split kernels computes the
 // plan itself into LDS at its start (the scan costs each workgroup less than
 // the separate launch it replaces); beyond it a one-workgroup launch writes the
 // plan to the workspace first.
 constexpr int kLdsPlanSeqs = 2048;
 
-// Up to this many sequences the shared-tile kernel computes plan entries from
-// the sequence table when it needs them (a scalar loop) instead of reading a
-// plan written by a separate launch.
-constexpr int kScanPlanSeqs = 16;
-
-// Work items of sequence s: query-row groups x KV heads x splits (the count
-// plan_scan sums).
-__device__ __forceinline__ int seq_items(const AttnSplitArgs& a, int s) {
-  const int q0 = ldc(a.qsl, s);
-  const int q_len = ldc(a.qsl, s + 1) - q0;
-  const SeqSplits sp = seq_splits(q_len, ldc(a.seq_lens, s), a.window, a.split, a.ns);
-  const int tq = (kRowsPerBlock >> a.log2_group) * a.qblocks;
-  return sp.n > 0 ? ((q_len + tq - 1) / tq) * a.num_kv_heads * sp.n : 0;
-}
-
 // Plan entry i (the first item of sequence i; the total at i = num_seqs), from
-// the workgroup's LDS copy, from the workspace, or computed on demand; all are
-// wave-uniform.
+// the workgroup's LDS copy or from the workspace; wave-uniform.
 struct PlanView {
-  const int* lds;  // nullptr: the workspace copy a.plan (or computed, with scan)
-  int scan;        // 1: entries computed from the sequence table (few sequences)
+  const int* lds;  // nullptr: the workspace copy a.plan
+  int lds_asm;     // 1: the LDS copy is read by a load the compiler does not see
   __device__ __forceinline__ int at(const AttnSplitArgs& a, int i) const {
-    if (scan) {
-      int c = 0;
-      for (int s = 0; s < i; ++s) c += seq_items(a, s);
-      return c;
+    if (lds && lds_asm) {
+      // In a kernel with copies to LDS in flight the compiler orders every
+      // LDS load after all of them; this table is written before the first
+      // copy and never again, so it is read by a load of its own that waits
+      // only for itself (and other LDS and scalar loads), in the same block.
+      int v;
+#if defined(__HIP_DEVICE_COMPILE__)
+      const uint32_t addr = (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) int*)(lds + i);
+      asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+#else
+      v = lds[i];
+#endif
+      return __builtin_amdgcn_readfirstlane(v);
     }
     return lds ? __builtin_amdgcn_readfirstlane(lds[i]) : ldc(a.plan, i);
   }
@@ -644,7 +637,7 @@ __global__ __launch_bounds__(64 * kSplitWaves, (QB == 1 && D <= 128) ? 2 : 1) vo
   __shared__ int carry_sh;
   SplitWave<D, QB> w{a};
   w.pv.lds = nullptr;
-  w.pv.scan = 0;
+  w.pv.lds_asm = 0;
   if (a.num_seqs <= kLdsPlanSeqs) {
     plan_scan<64 * kSplitWaves>(a, wave_tot, &carry_sh, [&](int i, int v) { plan_s[i] = v; });
     __syncthreads();
@@ -841,13 +834,21 @@ __global__ __launch_bounds__(64 * kSharedWaves, 2) void attn_split_shared_kernel
   __shared__ __attribute__((aligned(1024))) char ring[S::R * S::TILE];
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
-  // The plan comes from the workspace (scalar loads), or for a few sequences
-  // is computed from the sequence table on demand: an LDS copy would be read
-  // by ordinary LDS loads, which the compiler must order after every copy to
-  // LDS still in flight.
+  // The plan: up to kLdsPlanSeqs sequences every workgroup computes it into
+  // LDS before its first copy (read back with loads of their own, see
+  // PlanView), beyond that it comes from the workspace (scalar loads).
+  __shared__ int plan_s[kLdsPlanSeqs + 1];
+  __shared__ int wave_tot[kSharedWaves];
+  __shared__ int carry_sh;
   PlanView pv;
   pv.lds = nullptr;
-  pv.scan = a.num_seqs <= kScanPlanSeqs ? 1 : 0;
+  pv.lds_asm = 0;
+  if (a.num_seqs <= kLdsPlanSeqs) {
+    plan_scan<64 * kSharedWaves>(a, wave_tot, &carry_sh, [&](int i, int v) { plan_s[i] = v; });
+    __syncthreads();
+    pv.lds = plan_s;
+    pv.lds_asm = 1;
+  }
   const int total = pv.at(a, a.num_seqs);
   const int G = (int)gridDim.x;
   TileCursor cc, lc;
@@ -1559,7 +1560,7 @@ hipError_t shared_launch(AttnSplitArgs a, hipStream_t stream) {
   if (groups <= 0) return hipErrorInvalidDevice;
   // Workgroup g takes items g, g + G, ...: no more workgroups than items.
   groups = (int)std::min<int64_t>(groups, std::max<int64_t>(1, item_bound(a, kSharedBlocks)));
-  if (a.num_seqs > kScanPlanSeqs) {
+  if (a.num_seqs > kLdsPlanSeqs) {
     hipLaunchKernelGGL(attn_plan_kernel, dim3(1), dim3(1024), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
